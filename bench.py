@@ -1,0 +1,182 @@
+"""Benchmark of the M²RNN forward recurrence on one MI355X.
+
+One step = one full forward call over the whole workload batch (every
+(batch, head) unit, every time step), inputs already resident in HBM. Default
+workload: B=8, H=16, K=V=128, T=2048, bf16 inputs with an fp32 state (the
+K=V=128 configuration the headline metric is quoted on).
+
+Prints ONE JSON line (rank 0). Usage:
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload C3] [--algo auto]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense matrix-core peaks
+METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="C3")
+    ap.add_argument("--algo", default="auto")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time for the oracle baseline sample (0 disables)")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, x, budget_s):
+    """The fp64 oracle as it stands, on all units of the workload for a bounded
+    number of leading steps; throughput in tokens*heads/s (linear in T)."""
+    import numpy as np
+    from oracle import m2rnn_fwd_ref
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=None)
+    except Exception:
+        pass
+
+    def run(ts):
+        sub = {k: (None if v is None else (v[:, :, :ts] if k in ("k", "v", "q", "f") else v)) for k, v in x.items()}
+        t0 = time.perf_counter()
+        m2rnn_fwd_ref(sub["k"], sub["v"], sub["q"], sub["f"], sub["W"], sub["H0"], dtype=cfg.dtype)
+        return time.perf_counter() - t0
+
+    probe = min(8, cfg.T)
+    dt = run(probe)
+    ts = int(min(cfg.T, max(probe, probe * budget_s / max(dt, 1e-6))))
+    dt = run(ts)
+    return {
+        "value": cfg.B * cfg.H * ts / dt,
+        "unit": "tok·heads/s",
+        "cores": threads if threads else os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle, all {cfg.B * cfg.H} (b,h) units of {cfg.name}, first {ts} of {cfg.T} steps "
+                  f"({dt:.1f}s); matmul on OpenBLAS threads, elementwise single-threaded",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); units shard across GPUs "
+              "with no communication, so N GPUs run N independent copies of this measurement.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from non_linear_matrix_amd import m2rnn
+    from non_linear_matrix_amd.inputs import CONFIGS, generate
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    m2rnn.load()
+    cfg = CONFIGS[args.workload]
+    plan = m2rnn.get_plan(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V, cfg.dtype, args.algo)
+    print(f"[bench] workload {cfg} plan {plan}", file=sys.stderr, flush=True)
+    x = generate(cfg, args.seed)
+    dev = {}
+    for key, a in x.items():
+        if a is None:
+            dev[key] = None
+        elif a.dtype == np.uint16:
+            dev[key] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            dev[key] = torch.from_numpy(a).cuda()
+    y = torch.zeros((cfg.B, cfg.H, cfg.T, cfg.V), dtype=torch.float32, device="cuda")
+    HT = torch.empty((cfg.B, cfg.H, cfg.K, cfg.V), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    # When the kernel sums several workgroups' readouts into y, the step clears y
+    # itself (part of the timed work) and asks the library to accumulate, so the
+    # events below bracket the recurrence kernel alone.
+    clear_here = bool(plan["clears_y"])
+
+    def step(ev0=None, ev1=None):
+        if clear_here:
+            y.zero_()
+        if ev0 is not None:
+            ev0.record(stream)
+        m2rnn.fwd(dev["k"], dev["v"], dev["q"], dev["f"], dev["W"], dev["H0"], y=y, H_T=HT,
+                  algo=args.algo, stream=stream, accumulate_y=clear_here)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(*evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    ms_per_step = total_ms / args.steps
+    tokens = cfg.B * cfg.H * cfg.T
+    value = tokens / (ms_per_step * 1e-3)
+    flops = 2.0 * cfg.K * cfg.V * cfg.V * tokens          # H_{t-1} W per (b, h, t)
+    achieved = flops / (kern_avg * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tok·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} K={cfg.K} V={cfg.V} T={cfg.T}, "
+                        f"{cfg.dtype} inputs, fp32 state, seed {args.seed}",
+            "B": cfg.B, "H": cfg.H, "K": cfg.K, "V": cfg.V, "T": cfg.T,
+            "algo": plan["algo"], "grid": plan["grid"], "block": plan["block"],
+            "parallelism": "one GPU; (b,h) units x row groups across CUs",
+        },
+        "mfma_util_pct": 100.0 * achieved / peak,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "kernel": "mfma_fwd_kernel" if plan["algo"].startswith("mfma") else "simple_fwd_kernel",
+            "kernel_avg_ms": kern_avg,
+            "flops_per_launch": flops,
+        },
+        "wall_s": wall,
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * m2rnn.h — C ABI of the M²RNN forward recurrence for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (state update as in the gist.science technical summary of
+ * "M²RNN: Non-Linear RNNs with Matrix-Valued States for Scalable Language
+ * Modeling", §2.1 core architecture design, update equations; the same pair in
+ * the Japanese summary §2.1): for every (batch b, head h) independently, with
+ * a K x V state H and t = 1..T,
+ *
+ *     Z_t = tanh(H_{t-1} W_h + k_t v_t^T)
+ *     H_t = f_t H_{t-1} + (1 - f_t) Z_t
+ *     y_t = H_t^T q_t            (readout: not given on the pages; the reading
+ *                                 taken here uses the post-update state)
+ *
+ * W_h is the head's V x V transition matrix, multiplied from the right so that
+ * it mixes the value axis; f_t is one scalar gate per (b, h, t) in [0, 1],
+ * consumed as given (its parameterisation from the input is outside this call).
+ *
+ * Layouts (all contiguous, row-major, no strides):
+ *   k, q  [B][H][T][K]        in_dtype
+ *   v     [B][H][T][V]        in_dtype
+ *   f     [B][H][T]           in_dtype
+ *   W     [H][V][V]           in_dtype, (H W)[i][j] = sum_l H[i][l] * W[h][l][j]
+ *   H0    [B][H][K][V]        fp32, may be NULL (zero initial state)
+ *   y     [B][H][T][V]        fp32 output
+ *   H_T   [B][H][K][V]        fp32 output, may be NULL; may equal H0 (in-place
+ *                             continuation); no other overlap is allowed.
+ * in_dtype M2RNN_DTYPE_BF16 means every input element is a bfloat16 bit
+ * pattern (uint16); M2RNN_DTYPE_F32 means IEEE fp32.
+ *
+ * Pointers are device pointers (hipMalloc'd or equivalent), each 16-byte
+ * aligned. The caller owns every buffer and the stream. The library allocates
+ * nothing; calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream) and results are valid once the caller synchronises that stream.
+ * Before the recurrence kernel, a call may clear y with a fill kernel enqueued
+ * on the same stream. The library keeps no global mutable state and is safe to
+ * call from several host threads.
+ *
+ * Errors: arguments are validated on the host before any HIP call; a failed
+ * validation enqueues nothing. INVALID_VALUE: a required pointer (k, v, q, f,
+ * W, y) is NULL, a size is < 1, a pointer is not 16-byte aligned, or the
+ * element counts overflow 2^62. NOT_SUPPORTED: K or V is not one of 16, 32,
+ * ..., 128 (multiples of 16, the matrix-unit granularity the pages state in
+ * the zh summary §2.2), an unknown dtype or algorithm, or an algorithm that
+ * does not cover the requested shape/dtype. LAUNCH: the HIP launch reported
+ * an error. NaN/Inf inputs are not checked; they propagate.
+ */
+#ifndef M2RNN_H_
+#define M2RNN_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum m2rnn_status {
+  M2RNN_SUCCESS = 0,
+  M2RNN_ERROR_INVALID_VALUE = 1,
+  M2RNN_ERROR_NOT_SUPPORTED = 2,
+  M2RNN_ERROR_LAUNCH = 3
+} m2rnn_status;
+
+typedef enum m2rnn_dtype {
+  M2RNN_DTYPE_F32 = 0,
+  M2RNN_DTYPE_BF16 = 1
+} m2rnn_dtype;
+
+/* Kernel family.
+ * SIMPLE:     one workgroup per (b, h), fp32 arithmetic from LDS; covers every
+ *             supported shape and both dtypes (the fp32 path).
+ * MFMA:       bf16 inputs, K in {32, 64, 128}, V in {64, 128}; the fp32 state
+ *             stays in registers across all steps, H_{t-1} W runs on
+ *             v_mfma_f32_16x16x32_bf16 with the state rounded to bf16
+ *             (round-to-nearest-even) as the matrix operand and fp32
+ *             accumulation; rank-1 write, tanh, gate blend and readout are
+ *             fused in the same kernel. Fastest; per-step operand rounding of
+ *             2^-9 relative, which a sensitive trajectory can amplify.
+ * MFMA_SPLIT: as MFMA with the state operand split into bf16 hi + bf16 lo and
+ *             two MFMA passes (~2^-17 relative operand error).
+ * AUTO:       MFMA_SPLIT where it covers the shape, else SIMPLE. */
+typedef enum m2rnn_algo {
+  M2RNN_ALGO_AUTO = 0,
+  M2RNN_ALGO_SIMPLE = 1,
+  M2RNN_ALGO_MFMA = 2,
+  M2RNN_ALGO_MFMA_SPLIT = 3
+} m2rnn_algo;
+
+/* The forward recurrence with the automatically chosen kernel. */
+m2rnn_status m2rnn_fwd(const void* k, const void* v, const void* q, const void* f, const void* W,
+                       const float* H0, float* y, float* H_T,
+                       int B, int H, int T, int K, int V, m2rnn_dtype in_dtype, void* stream);
+
+/* The same with an explicit kernel family (for tests and measurements). */
+m2rnn_status m2rnn_fwd_algo(const void* k, const void* v, const void* q, const void* f, const void* W,
+                            const float* H0, float* y, float* H_T,
+                            int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, void* stream);
+
+/* Flags for m2rnn_fwd_ex. */
+enum {
+  /* Add the readout into y instead of overwriting it: y[b][h][t][:] += H_t^T q_t.
+   * The library then never clears y itself, so a caller that zeroes y first
+   * gets the plain result with the recurrence as the only kernel on the stream. */
+  M2RNN_FLAG_ACCUMULATE_Y = 1u
+};
+
+/* m2rnn_fwd_algo with flags (a bitwise OR of M2RNN_FLAG_*; unknown bits are
+ * NOT_SUPPORTED). */
+m2rnn_status m2rnn_fwd_ex(const void* k, const void* v, const void* q, const void* f, const void* W,
+                          const float* H0, float* y, float* H_T,
+                          int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                          m2rnn_algo algo, unsigned flags, void* stream);
+
+/* Host-only argument check: returns exactly what m2rnn_fwd_algo would return
+ * before launching, without touching the GPU. */
+m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const void* f, const void* W,
+                              const float* H0, const float* y, const float* H_T,
+                              int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                              m2rnn_algo algo);
+
+/* The kernel family AUTO resolves to for a shape (never AUTO; host only). */
+m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype);
+
+/* Launch plan of one call (host only, no GPU access). */
+typedef struct m2rnn_plan {
+  int algo;             /* resolved m2rnn_algo (never AUTO) */
+  int grid;             /* workgroups of the recurrence kernel */
+  int block;            /* threads per workgroup */
+  int rows_per_group;   /* state rows (of K) one workgroup carries */
+  int groups_per_unit;  /* workgroups sharing one (b, h); their readouts are summed into y */
+  int clears_y;         /* 1 if a call without M2RNN_FLAG_ACCUMULATE_Y enqueues a fill of y first */
+  int lds_bytes;        /* LDS per workgroup */
+} m2rnn_plan;
+
+/* Fill *plan for a call with these arguments. INVALID_VALUE for a NULL plan or
+ * sizes < 1; NOT_SUPPORTED as m2rnn_check_args. */
+m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, m2rnn_plan* plan);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* m2rnn_status_string(m2rnn_status status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int m2rnn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M2RNN_H_ */

@@ -1,0 +1,141 @@
+// C ABI of the M²RNN forward recurrence: host-side validation and dispatch.
+// Validation touches no HIP API, so every error path runs without a GPU.
+#include "m2rnn.h"
+
+#include <cstdint>
+
+#include "m2rnn_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<std::uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dim(int d) { return d >= 16 && d <= 128 && (d % 16) == 0; }
+
+// element counts must stay far below 2^62 so 64-bit index arithmetic cannot wrap
+bool counts_fit(int B, int H, int T, int K, int V) {
+  const long double lim = 4.0e18L;
+  long double bh = (long double)B * H;
+  long double n1 = bh * T * (K > V ? K : V);
+  long double n2 = bh * K * V;
+  long double n3 = (long double)H * V * V;
+  return n1 < lim && n2 < lim && n3 < lim;
+}
+
+m2rnn_status check(const void* k, const void* v, const void* q, const void* f, const void* W,
+                   const float* H0, const float* y, const float* HT, int B, int H, int T, int K,
+                   int V, m2rnn_dtype dt, m2rnn_algo algo) {
+  if (!k || !v || !q || !f || !W || !y) return M2RNN_ERROR_INVALID_VALUE;
+  if (B < 1 || H < 1 || T < 1 || K < 1 || V < 1) return M2RNN_ERROR_INVALID_VALUE;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(f) || !aligned16(W) ||
+      !aligned16(y) || (H0 && !aligned16(H0)) || (HT && !aligned16(HT)))
+    return M2RNN_ERROR_INVALID_VALUE;
+  if (!counts_fit(B, H, T, K, V)) return M2RNN_ERROR_INVALID_VALUE;
+  if (dt != M2RNN_DTYPE_F32 && dt != M2RNN_DTYPE_BF16) return M2RNN_ERROR_NOT_SUPPORTED;
+  if (!supported_dim(K) || !supported_dim(V)) return M2RNN_ERROR_NOT_SUPPORTED;
+  switch (algo) {
+    case M2RNN_ALGO_AUTO:
+    case M2RNN_ALGO_SIMPLE:
+      return M2RNN_SUCCESS;
+    case M2RNN_ALGO_MFMA:
+    case M2RNN_ALGO_MFMA_SPLIT:
+      return m2rnn::mfma_supports(K, V, dt == M2RNN_DTYPE_BF16) ? M2RNN_SUCCESS
+                                                                 : M2RNN_ERROR_NOT_SUPPORTED;
+    default:
+      return M2RNN_ERROR_NOT_SUPPORTED;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const void* f,
+                              const void* W, const float* H0, const float* y, const float* H_T,
+                              int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                              m2rnn_algo algo) {
+  return check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
+}
+
+m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype) {
+  (void)B;
+  (void)H;
+  (void)T;
+  if (m2rnn::mfma_supports(K, V, in_dtype == M2RNN_DTYPE_BF16)) return M2RNN_ALGO_MFMA_SPLIT;
+  return M2RNN_ALGO_SIMPLE;
+}
+
+m2rnn_status m2rnn_fwd_ex(const void* k, const void* v, const void* q, const void* f,
+                          const void* W, const float* H0, float* y, float* H_T, int B, int H,
+                          int T, int K, int V, m2rnn_dtype in_dtype, m2rnn_algo algo,
+                          unsigned flags, void* stream) {
+  m2rnn_status st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
+  if (st != M2RNN_SUCCESS) return st;
+  if ((flags & ~static_cast<unsigned>(M2RNN_FLAG_ACCUMULATE_Y)) != 0u) return M2RNN_ERROR_NOT_SUPPORTED;
+  if (algo == M2RNN_ALGO_AUTO) algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
+  m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype == M2RNN_DTYPE_BF16 ? 1 : 0,
+                   (flags & M2RNN_FLAG_ACCUMULATE_Y) ? 1 : 0};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT)
+    e = m2rnn::launch_mfma(a, algo == M2RNN_ALGO_MFMA_SPLIT, s);
+  else
+    e = m2rnn::launch_simple(a, s);
+  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+}
+
+m2rnn_status m2rnn_fwd_algo(const void* k, const void* v, const void* q, const void* f,
+                            const void* W, const float* H0, float* y, float* H_T, int B, int H,
+                            int T, int K, int V, m2rnn_dtype in_dtype, m2rnn_algo algo,
+                            void* stream) {
+  return m2rnn_fwd_ex(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo, 0u, stream);
+}
+
+m2rnn_status m2rnn_fwd(const void* k, const void* v, const void* q, const void* f, const void* W,
+                       const float* H0, float* y, float* H_T, int B, int H, int T, int K, int V,
+                       m2rnn_dtype in_dtype, void* stream) {
+  return m2rnn_fwd_algo(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, M2RNN_ALGO_AUTO,
+                        stream);
+}
+
+m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, m2rnn_plan* plan) {
+  if (!plan) return M2RNN_ERROR_INVALID_VALUE;
+  const void* p = reinterpret_cast<const void*>(static_cast<std::uintptr_t>(0x10000));
+  const float* pf = static_cast<const float*>(p);
+  m2rnn_status st = check(p, p, p, p, p, nullptr, pf, nullptr, B, H, T, K, V, in_dtype, algo);
+  if (st != M2RNN_SUCCESS) return st;
+  if (algo == M2RNN_ALGO_AUTO) algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
+  m2rnn::Plan pl = (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT)
+                       ? m2rnn::plan_mfma(B, H, K, V, algo == M2RNN_ALGO_MFMA_SPLIT)
+                       : m2rnn::plan_simple(B, H, K, V);
+  if (pl.grid < 0) return M2RNN_ERROR_INVALID_VALUE;
+  plan->algo = algo;
+  plan->grid = pl.grid;
+  plan->block = pl.block;
+  plan->rows_per_group = pl.rows_per_group;
+  plan->groups_per_unit = pl.groups_per_unit;
+  plan->clears_y = pl.clears_y;
+  plan->lds_bytes = pl.lds_bytes;
+  return M2RNN_SUCCESS;
+}
+
+const char* m2rnn_status_string(m2rnn_status status) {
+  switch (status) {
+    case M2RNN_SUCCESS:
+      return "success";
+    case M2RNN_ERROR_INVALID_VALUE:
+      return "invalid value (null pointer, size < 1, misaligned pointer or size overflow)";
+    case M2RNN_ERROR_NOT_SUPPORTED:
+      return "not supported (K or V not in {16, 32, ..., 128}, unknown dtype or algorithm, "
+             "or an algorithm that does not cover the shape)";
+    case M2RNN_ERROR_LAUNCH:
+      return "kernel launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+int m2rnn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+"""Python binding of libm2rnn.so (ctypes). Argument marshalling only.
+
+Every step of the recurrence runs in the library's HIP kernels; PyTorch is used
+here for device buffers and the current stream. If the library is not built,
+every call raises — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "LIB_PATH", "M2RNNError", "load", "fwd", "check_args", "pick_algo", "status_string", "version",
+    "STATUS", "ALGOS", "DTYPES", "declared_functions", "get_plan", "Plan", "FLAG_ACCUMULATE_Y",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm2rnn.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "m2rnn.h")
+
+STATUS = {0: "M2RNN_SUCCESS", 1: "M2RNN_ERROR_INVALID_VALUE", 2: "M2RNN_ERROR_NOT_SUPPORTED", 3: "M2RNN_ERROR_LAUNCH"}
+ALGOS = {"auto": 0, "simple": 1, "mfma": 2, "mfma_split": 3}
+DTYPES = {"f32": 0, "bf16": 1}
+FLAG_ACCUMULATE_Y = 1
+
+_lib = None
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int), ("grid", ctypes.c_int), ("block", ctypes.c_int),
+                ("rows_per_group", ctypes.c_int), ("groups_per_unit", ctypes.c_int),
+                ("clears_y", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+
+
+def get_plan(B: int, H: int, T: int, K: int, V: int, dtype: str, algo: str = "auto") -> dict:
+    """The launch plan the library would use (host only)."""
+    p = Plan()
+    st = load().m2rnn_get_plan(B, H, T, K, V, DTYPES[dtype], ALGOS[algo], ctypes.byref(p))
+    if st != 0:
+        raise M2RNNError(st, "m2rnn_get_plan")
+    d = {name: getattr(p, name) for name, _ in Plan._fields_}
+    d["algo"] = {v: k for k, v in ALGOS.items()}[d["algo"]]
+    return d
+
+
+class M2RNNError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libm2rnn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m non_linear_matrix_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+    lib.m2rnn_fwd.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, vp]
+    lib.m2rnn_fwd.restype = i
+    lib.m2rnn_fwd_algo.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i, vp]
+    lib.m2rnn_fwd_algo.restype = i
+    lib.m2rnn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i, ctypes.c_uint, vp]
+    lib.m2rnn_fwd_ex.restype = i
+    lib.m2rnn_check_args.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i]
+    lib.m2rnn_check_args.restype = i
+    lib.m2rnn_pick_algo.argtypes = [i, i, i, i, i, i]
+    lib.m2rnn_pick_algo.restype = i
+    lib.m2rnn_status_string.argtypes = [i]
+    lib.m2rnn_status_string.restype = ctypes.c_char_p
+    lib.m2rnn_get_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.m2rnn_get_plan.restype = i
+    lib.m2rnn_version.argtypes = []
+    lib.m2rnn_version.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().m2rnn_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().m2rnn_version())
+
+
+def pick_algo(B: int, H: int, T: int, K: int, V: int, dtype: str) -> str:
+    code = load().m2rnn_pick_algo(B, H, T, K, V, DTYPES[dtype])
+    return {v: k for k, v in ALGOS.items()}[code]
+
+
+def check_args(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, dtype, algo="auto") -> int:
+    """Host-only validation on raw addresses (ints or None); returns the status code."""
+    return int(load().m2rnn_check_args(k, v, q, f, W, H0, y, H_T, B, H, T, K, V,
+                                       DTYPES.get(dtype, dtype) if isinstance(dtype, str) else dtype,
+                                       ALGOS.get(algo, algo) if isinstance(algo, str) else algo))
+
+
+def declared_functions() -> list:
+    """Names of the functions include/m2rnn.h declares."""
+    import re
+    with open(HEADER_PATH) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(m2rnn_\w+)\s*\(", text)))
+
+
+def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, algo: str = "auto", stream=None,
+        want_state: bool = True, accumulate_y: bool = False) -> Tuple["object", Optional["object"]]:
+    """Run the forward recurrence on torch device tensors.
+
+    k, q [B,H,T,K]; v [B,H,T,V]; f [B,H,T]; W [H,V,V] — all torch.bfloat16 or all
+    torch.float32; H0 [B,H,K,V] float32 or None. y / H_T may be given (float32,
+    contiguous) to write into; otherwise they are allocated with torch.
+    Returns (y, H_T) (H_T is None when want_state is False and none was given).
+    accumulate_y adds the readout into the given y (M2RNN_FLAG_ACCUMULATE_Y).
+    """
+    import torch
+
+    lib = load()
+    if k.dtype == torch.bfloat16:
+        dt = DTYPES["bf16"]
+    elif k.dtype == torch.float32:
+        dt = DTYPES["f32"]
+    else:
+        raise TypeError(f"unsupported input dtype {k.dtype}")
+    for name, t in (("v", v), ("q", q), ("f", f), ("W", W)):
+        if t.dtype != k.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {k.dtype}")
+    tensors = [k, v, q, f, W] + [t for t in (H0, y, H_T) if t is not None]
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    if k.dim() != 4 or v.dim() != 4 or q.shape != k.shape or f.dim() != 3 or W.dim() != 3:
+        raise ValueError("expected k,q [B,H,T,K], v [B,H,T,V], f [B,H,T], W [H,V,V]")
+    B, H, T, K = k.shape
+    V = v.shape[-1]
+    if tuple(v.shape) != (B, H, T, V) or tuple(f.shape) != (B, H, T) or tuple(W.shape) != (H, V, V):
+        raise ValueError("inconsistent shapes")
+    if H0 is not None and (H0.dtype != torch.float32 or tuple(H0.shape) != (B, H, K, V)):
+        raise ValueError("H0 must be float32 [B,H,K,V]")
+    if accumulate_y and y is None:
+        raise ValueError("accumulate_y needs y")
+    if y is None:
+        y = torch.empty((B, H, T, V), dtype=torch.float32, device=k.device)
+    elif y.dtype != torch.float32 or tuple(y.shape) != (B, H, T, V):
+        raise ValueError("y must be float32 [B,H,T,V]")
+    if H_T is None and want_state:
+        H_T = torch.empty((B, H, K, V), dtype=torch.float32, device=k.device)
+    elif H_T is not None and (H_T.dtype != torch.float32 or tuple(H_T.shape) != (B, H, K, V)):
+        raise ValueError("H_T must be float32 [B,H,K,V]")
+    if stream is None:
+        stream = torch.cuda.current_stream(k.device)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.m2rnn_fwd_ex(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(y), ptr(H_T),
+                          B, H, T, K, V, dt, ALGOS[algo], FLAG_ACCUMULATE_Y if accumulate_y else 0,
+                          stream.cuda_stream)
+    if st != 0:
+        raise M2RNNError(st, "m2rnn_fwd")
+    return y, H_T

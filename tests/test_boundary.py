@@ -1,0 +1,133 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every declared
+symbol, and its argument validation returns the documented codes without
+touching the GPU."""
+import ctypes
+import os
+
+import pytest
+
+from non_linear_matrix_amd import m2rnn
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+A = 0x10000  # a 16-byte aligned fake device address; validation never dereferences it
+
+
+def _args(**over):
+    base = dict(k=A, v=A + 0x100, q=A + 0x200, f=A + 0x300, W=A + 0x400, H0=None, y=A + 0x500,
+                H_T=A + 0x600, B=2, H=3, T=5, K=64, V=128, dtype="bf16", algo="auto")
+    base.update(over)
+    return base
+
+
+def _check(**over):
+    a = _args(**over)
+    return m2rnn.check_args(a["k"], a["v"], a["q"], a["f"], a["W"], a["H0"], a["y"], a["H_T"],
+                            a["B"], a["H"], a["T"], a["K"], a["V"], a["dtype"], a["algo"])
+
+
+def test_library_exists_and_loads():
+    assert os.path.exists(m2rnn.LIB_PATH), "build the library first (python -m non_linear_matrix_amd.build)"
+    lib = m2rnn.load()
+    assert m2rnn.version() == 100
+
+
+def test_every_declared_symbol_is_exported():
+    names = m2rnn.declared_functions()
+    assert set(names) >= {"m2rnn_fwd", "m2rnn_fwd_algo", "m2rnn_check_args", "m2rnn_pick_algo",
+                          "m2rnn_status_string", "m2rnn_version"}
+    raw = ctypes.CDLL(m2rnn.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), f"{name} declared in include/m2rnn.h but not exported"
+
+
+def test_status_strings_cover_every_code():
+    seen = set()
+    for code in (0, 1, 2, 3):
+        s = m2rnn.status_string(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 4
+    assert m2rnn.status_string(99) == "unknown status"
+
+
+def test_valid_arguments_pass():
+    assert _check() == OK
+    assert _check(H0=A + 0x700, H_T=None) == OK
+    assert _check(dtype="f32", K=16, V=16, algo="simple") == OK
+    assert _check(K=128, V=128, algo="mfma") == OK
+
+
+@pytest.mark.parametrize("name", ["k", "v", "q", "f", "W", "y"])
+def test_null_required_pointer(name):
+    assert _check(**{name: None}) == INVALID
+
+
+@pytest.mark.parametrize("name", ["k", "v", "q", "f", "W", "y", "H0", "H_T"])
+def test_misaligned_pointer(name):
+    assert _check(**{name: A + 0x800 + 4}) == INVALID
+
+
+@pytest.mark.parametrize("name", ["B", "H", "T", "K", "V"])
+@pytest.mark.parametrize("value", [0, -1])
+def test_bad_sizes(name, value):
+    assert _check(**{name: value}) == INVALID
+
+
+@pytest.mark.parametrize("K,V", [(8, 64), (64, 8), (20, 64), (64, 20), (144, 64), (64, 144), (1, 1)])
+def test_unsupported_dims(K, V):
+    assert _check(K=K, V=V) == UNSUPPORTED
+
+
+def test_size_overflow_is_rejected():
+    assert _check(B=2 ** 30, H=2 ** 30, T=2 ** 30) == INVALID
+
+
+def test_unknown_dtype_and_algo():
+    assert _check(dtype=7) == UNSUPPORTED
+    assert _check(algo=9) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("algo", ["mfma", "mfma_split"])
+def test_mfma_coverage(algo):
+    assert _check(dtype="f32", algo=algo) == UNSUPPORTED          # fp32 inputs: simple kernel only
+    assert _check(K=16, V=128, algo=algo) == UNSUPPORTED          # fewer than 32 rows
+    assert _check(K=96, V=128, algo=algo) == UNSUPPORTED          # more than two row groups
+    assert _check(K=128, V=96, algo=algo) == UNSUPPORTED
+    for K in (32, 64, 128):
+        for V in (64, 128):
+            assert _check(K=K, V=V, algo=algo) == OK
+
+
+def test_launch_plans():
+    p = m2rnn.get_plan(8, 16, 2048, 128, 128, "bf16", "auto")
+    assert p["algo"] == "mfma_split" and p["grid"] == 256 and p["block"] == 256
+    assert p["rows_per_group"] == 64 and p["groups_per_unit"] == 2 and p["clears_y"] == 1
+    assert p["lds_bytes"] <= 160 * 1024
+    p = m2rnn.get_plan(2, 16, 32768, 64, 128, "bf16", "mfma")
+    assert p["grid"] == 32 and p["groups_per_unit"] == 1 and p["clears_y"] == 0
+    p = m2rnn.get_plan(1, 1, 64, 16, 16, "f32", "auto")
+    assert p["algo"] == "simple" and p["grid"] == 1
+    with pytest.raises(m2rnn.M2RNNError):
+        m2rnn.get_plan(1, 1, 64, 20, 16, "f32", "auto")
+
+
+def test_unknown_flag_bits_are_rejected():
+    lib = m2rnn.load()
+    st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 1, 4, 64, 64, 1, 0, 2, None)
+    assert st == UNSUPPORTED
+    st = lib.m2rnn_fwd_ex(None, A, A, A, A, None, A, None, 1, 1, 4, 64, 64, 1, 0, 1, None)
+    assert st == INVALID
+
+
+def test_auto_picks_a_kernel_that_covers_the_shape():
+    assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "bf16") == "mfma_split"
+    assert m2rnn.pick_algo(1, 1, 64, 16, 16, "f32") == "simple"
+    assert m2rnn.pick_algo(1, 1, 64, 16, 128, "bf16") == "simple"
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 1, 2, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        m2rnn.fwd(x, x, x, torch.zeros((1, 1, 2), dtype=torch.bfloat16),
+                  torch.zeros((1, 16, 16), dtype=torch.bfloat16))
