@@ -29,6 +29,8 @@ def command(out: str) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 VALU forms are kept out of the device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results land in arch VGPRs, where the fused epilogue reads them
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC] + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out]
 
 

@@ -243,7 +243,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
           const int row = 32 * b + 16 * (j / 4) + 4 * g + (j % 4);
           t[j] = static_cast<short>(Wp[row * V + 16 * c + n]);
         }
-        Wf[c][b] = __builtin_bit_cast(bf16x8, t);
+        // pin the fragment to the accumulation registers: it is only ever a
+        // matrix operand, and this leaves the arch VGPRs to the epilogue
+        u4 wa = __builtin_bit_cast(u4, t);
+        asm volatile("" : "=a"(wa) : "0"(wa));
+        Wf[c][b] = __builtin_bit_cast(bf16x8, wa);
       }
   }
 
@@ -330,47 +334,42 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     }
   };
 
-  __syncthreads();
-
-  for (int t = 0; t < T; ++t) {
+  // One step, software-pipelined across steps: `cur` holds the finished
+  // H_{t-1} W of step t; as soon as the epilogue has produced state tiles 2b and
+  // 2b+1 (the next operand block b), the MFMAs of step t+1 for block b are issued
+  // into `nxt`, so the matrix cores work on step t+1 while the VALU finishes step t.
+  auto step = [&](int t, f4 (&cur)[CT], f4 (&nxt)[CT]) {
     const int s = t % kChunk;
     const int sb = (t / kChunk) & 1;
-    // H_{t-1} W on the matrix cores
-    f4 acc[CT];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      acc[c] = f4{0, 0, 0, 0};
-#pragma unroll
-      for (int b = 0; b < KB; ++b) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bf[b], acc[c], 0, 0, 0);
-      if constexpr (SPLIT) {
-#pragma unroll
-        for (int b = 0; b < KB; ++b) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bl[b], acc[c], 0, 0, 0);
-      }
-    }
-    if (t > 0) readout(t - 1);
-    // rank-1 write, tanh, gate blend
     const float* fs = fs_all + (sb * kChunk + s) * 4;
     const float fg = fs[0], av = fs[1], m2a = fs[2];
     const float ck = ks_all[(sb * kChunk + s) * R + 16 * w + n];
     const float* vrow = vs_all + (sb * kChunk + s) * V;
+    unsigned short* hdst = Hs + (t & 1) * R * HROW + (16 * w + n) * HROW + 8 * g;
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const f4 vv = *reinterpret_cast<const f4*>(vrow + 16 * c + 4 * g);
+    for (int b = 0; b < KB; ++b) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float u = fmaf(ck, vv[i], acc[c][i]);
-        const float e = __builtin_amdgcn_exp2f(u);
-        const float r = __builtin_amdgcn_rcpf(1.0f + e);
-        G[c][i] = fmaf(m2a, r, fmaf(fg, G[c][i], av));
+      for (int c = 2 * b; c < 2 * b + 2; ++c) {
+        const f4 vv = *reinterpret_cast<const f4*>(vrow + 16 * c + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // rank-1 write, tanh via exp2/rcp, gate blend
+          const float u = fmaf(ck, vv[i], cur[c][i]);
+          const float e = __builtin_amdgcn_exp2f(u);
+          const float r = __builtin_amdgcn_rcpf(1.0f + e);
+          G[c][i] = fmaf(m2a, r, fmaf(fg, G[c][i], av));
+        }
       }
-    }
+      make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
+      // rounded state block -> LDS for the readout (row 16w + n, positions 32b + 8g)
+      *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
 #pragma unroll
-    for (int b = 0; b < KB; ++b) make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
-    // rounded state tile -> LDS for the readout (row 16w + n, positions 32b + 8g)
-    {
-      unsigned short* dst = Hs + (t & 1) * R * HROW + (16 * w + n) * HROW + 8 * g;
-#pragma unroll
-      for (int b = 0; b < KB; ++b) *reinterpret_cast<bf16x8*>(dst + 32 * b) = Bf[b];
+      for (int c = 0; c < CT; ++c) {
+        const f4 c_in = (b == 0) ? f4{0, 0, 0, 0} : nxt[c];
+        nxt[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bf[b], c_in, 0, 0, 0);
+        if constexpr (SPLIT) nxt[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bl[b], nxt[c], 0, 0, 0);
+      }
+      if (b == 0 && t > 0) readout(t - 1);
     }
     // chunk boundary: publish the prefetched chunk, start the next load
     if (s == kChunk - 1) {
@@ -381,7 +380,27 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
       }
     }
     __syncthreads();
+  };
+
+  // prologue: H_0 W for step 0
+  f4 accA[CT], accB[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    accA[c] = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      accA[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bf[b], accA[c], 0, 0, 0);
+      if constexpr (SPLIT) accA[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bl[b], accA[c], 0, 0, 0);
+    }
   }
+  __syncthreads();
+
+  int t = 0;
+  for (; t + 1 < T; t += 2) {
+    step(t, accA, accB);
+    step(t + 1, accB, accA);
+  }
+  if (t < T) step(t, accA, accB);
   readout(T - 1);
 
   if (a.HT) {
