@@ -313,28 +313,33 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 
   auto sbuf = [](int tt) { return (tt / kChunk) % NSB; };
 
-  // rank-1 write of step tt as the initial accumulator: acc[c] = (v_tt, tile c) x (hi, lo of c k_tt)
-  auto rank1_init = [&](int tt, f4 (&acc)[CT]) {
+  // rank-1 write of step tt as the initial accumulator: acc[c] = (v_tt, tile c) x (hi, lo of c k_tt).
+  // Operands are fetched one step ahead (R1 holds them in registers).
+  struct R1 {
+    unsigned int kpair;
+    u4 win[CT / 2];  // window k: packed pairs 2k .. 2k+3 (tiles 2k, 2k+1 use dword 0 / 1)
+  };
+  auto rank1_load = [&](int tt) {
+    R1 r;
     const int s = tt % kChunk, sb = sbuf(tt);
     const unsigned int* kp = (g == 0) ? kx_all + (sb * kChunk + s) * R + 16 * w + n : zero_lds;
-    const unsigned int kpair = *kp;
-    const u4 bx0 = u4{kpair, 0u, 0u, 0u};
-    const u4 bx1 = u4{0u, kpair, 0u, 0u};
-    const u4* vp = reinterpret_cast<const u4*>(vx_all + ((sb * kChunk + s) * 16 + n) * NVX);
-    u4 vw[NVX / 4];
+    r.kpair = *kp;
+    const unsigned int* vp = vx_all + ((sb * kChunk + s) * 16 + n) * NVX;
 #pragma unroll
-    for (int i = 0; i < NVX / 4; ++i) vw[i] = vp[i];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      // A window: 4 packed pairs starting at the even index c & ~1; the B pair
-      // sits in dword 0 (even c) or dword 1 (odd c), so only pair c contributes
-      const int base = c & ~1;
-      u4 win;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) win[d] = vw[(base + d) / 4][(base + d) % 4];
-      acc[c] = mfma(__builtin_bit_cast(bf16x8, win), __builtin_bit_cast(bf16x8, (c & 1) ? bx1 : bx0),
-                    f4{0, 0, 0, 0});
+    for (int k = 0; k < CT / 2; ++k) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(vp + 2 * k);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vp + 2 * k + 2);
+      r.win[k] = u4{lo.x, lo.y, hi.x, hi.y};
     }
+    return r;
+  };
+  auto rank1_init = [&](const R1& r, f4 (&acc)[CT]) {
+    const u4 bx0 = u4{r.kpair, 0u, 0u, 0u};
+    const u4 bx1 = u4{0u, r.kpair, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      acc[c] = mfma(__builtin_bit_cast(bf16x8, r.win[c / 2]), __builtin_bit_cast(bf16x8, (c & 1) ? bx1 : bx0),
+                    f4{0, 0, 0, 0});
   };
 
   // readout partials: Dr[P] lane (g, n) accumulates y_{t0 + n}[position 16 P + 4 g + i]
@@ -432,19 +437,37 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     }
   };
 
+  // per-step operands fetched one step ahead: the gate scalars of step t and the
+  // rank-1 operands of step t + 1
+  struct Pre {
+    f4 fs;
+    R1 r1;
+  };
+  auto prefetch = [&](int t) {
+    Pre q;
+    const int tt = t < T ? t : T - 1;
+    q.fs = *reinterpret_cast<const f4*>(fs_all + (sbuf(tt) * kChunk + tt % kChunk) * 4);
+    // the two-pass variant has no registers to spare: it fetches at use instead
+    if constexpr (!SPLIT) q.r1 = rank1_load(t + 1 < T ? t + 1 : T - 1);
+    return q;
+  };
+
   // One step. On entry `cur` holds c (G_{t-1} W + k_t v_t^T) except the last
   // operand block's share for tiles 2.., which phase 0 adds. Step t+1's
   // accumulators `nxt` start from its rank-1 write and take operand block b
   // right after the epilogue has produced it; block KB-1 is finished for tiles
   // 0, 1 here and for the other tiles in the next step's phase 0.
-  auto step = [&](int t, f4 (&cur)[CT], f4 (&nxt)[CT], bool even) {
-    const int s = t % kChunk, sb = sbuf(t);
-    const float* fs = fs_all + (sb * kChunk + s) * 4;
-    const float fg = fs[0], av = fs[1], m2a = fs[2];
+  auto step = [&](int t, f4 (&cur)[CT], f4 (&nxt)[CT], bool even, Pre& pre) {
+    const int s = t % kChunk;
+    const float fg = pre.fs[0], av = pre.fs[1], m2a = pre.fs[2];
     unsigned short* hdst = hb_w + (t & (NHS - 1)) * 16 * HROW + n * HROW + 8 * g;
     // phase 0
     products(KB - 1, 2, CT, cur);
-    rank1_init(t + 1 < T ? t + 1 : t, nxt);
+    if constexpr (SPLIT)
+      rank1_init(rank1_load(t + 1 < T ? t + 1 : t), nxt);
+    else
+      rank1_init(pre.r1, nxt);
+    pre = prefetch(t + 1);
     epilogue(0, cur, fg, av, m2a, hdst);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -460,17 +483,18 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 
   // prologue: c (H_0 W + k_0 v_0^T) for step 0, last operand block for tiles 0, 1 only
   f4 accA[CT], accB[CT];
-  rank1_init(0, accA);
+  rank1_init(rank1_load(0), accA);
 #pragma unroll
   for (int b = 0; b < KB - 1; ++b) products(b, 0, CT, accA);
   products(KB - 1, 0, 2, accA);
 
+  Pre pre = prefetch(0);
   int t = 0;
   for (; t + 1 < T; t += 2) {
-    step(t, accA, accB, true);
-    step(t + 1, accB, accA, false);
+    step(t, accA, accB, true, pre);
+    step(t + 1, accB, accA, false, pre);
   }
-  if (t < T) step(t, accA, accB, true);
+  if (t < T) step(t, accA, accB, true, pre);
 
   if (a.HT) {
     float* HT = a.HT + (unit * a.K + my_row) * V;
