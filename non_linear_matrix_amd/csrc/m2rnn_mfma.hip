@@ -74,10 +74,12 @@ constexpr int kChunk = 16;                     // steps staged per LDS chunk
 
 __device__ __forceinline__ float bf16_to_f32(unsigned int b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ unsigned int f32_to_bf16_rne(float x) {
-  const unsigned int u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __attribute__((ext_vector_type(2))) float f2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32: round to nearest even)
+__device__ __forceinline__ unsigned int pack_bf16(float x0, float x1) {
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f2{x0, x1}, bf16x2));
 }
 
 template <int V, int NW>
@@ -166,13 +168,15 @@ struct Stager {
         const int s = slot / (L::R / 8), part = slot % (L::R / 8);
         u4 lo4, hi4;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const unsigned int raw = (r[i / 2] >> (16 * (i % 2))) & 0xffffu;
-          const float ck = bf16_to_f32(raw) * kC;
-          const unsigned int hb = f32_to_bf16_rne(ck);
-          const unsigned int lb = f32_to_bf16_rne(ck - bf16_to_f32(hb));
-          const unsigned int pr = hb | (lb << 16);
-          if (i < 4) lo4[i] = pr; else hi4[i - 4] = pr;
+        for (int d = 0; d < 4; ++d) {
+          // elements 2d, 2d+1: c k rounded to bf16 (hi) and the exact residual rounded (lo)
+          const float ck0 = __uint_as_float(r[d] << 16) * kC;
+          const float ck1 = __uint_as_float(r[d] & 0xffff0000u) * kC;
+          const unsigned int hp = pack_bf16(ck0, ck1);
+          const unsigned int lp = pack_bf16(ck0 - __uint_as_float(hp << 16), ck1 - __uint_as_float(hp & 0xffff0000u));
+          const unsigned int p0 = (hp & 0xffffu) | (lp << 16);
+          const unsigned int p1 = (hp >> 16) | (lp & 0xffff0000u);
+          if (d < 2) { lo4[2 * d] = p0; lo4[2 * d + 1] = p1; } else { hi4[2 * d - 4] = p0; hi4[2 * d - 3] = p1; }
         }
         *reinterpret_cast<u4*>(kx + s * L::R + 8 * part) = lo4;
         *reinterpret_cast<u4*>(kx + s * L::R + 8 * part + 4) = hi4;
@@ -220,6 +224,15 @@ __device__ __forceinline__ void make_operand(const f4& g0, const f4& g1, bf16x8&
     }
     lo = __builtin_convertvector(r, bf16x8);
   }
+}
+
+// Workgroup barrier that orders LDS only. Global loads (the chunk prefetch) and
+// the atomic y updates stay in flight across it; a full __syncthreads would
+// wait for them, i.e. for a whole HBM round trip at every chunk end.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
@@ -374,43 +387,53 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   float* y = a.y;
   const bool atomic_y = splits > 1 || a.accumulate;
 
-  // chunk end after step tt: read out the pending step(s), sum the waves' partial
-  // readouts, store y, publish the chunk after next; two workgroup barriers
-  auto chunk_end = [&](int tt) {
-    if (tt & 1) readout(tt - 1, true, true);
-    else readout(tt, true, false);
-    const int t0 = tt - tt % kChunk;
-    const int nsteps = tt - t0 + 1;
+  // y for the steps t0 .. t0 + nsteps - 1 of one chunk from the summed partials
+  auto ysum_group = [&](int t0, int grp) {
+    const int sn = grp / (V / 4), pos = 4 * (grp % (V / 4));
+    f4 sum = *reinterpret_cast<const f4*>(yp_all + sn * V + pos);
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(yp_all + (ww * kChunk + sn) * V + pos);
+    sum *= kInvC;
+    // position 16 P + 4 gg  ->  column 32 (P/2) + 16 (gg%2) + 8 (P%2) + 4 (gg/2)
+    const int P = pos / 16, gg = (pos % 16) / 4;
+    const int col = 32 * (P / 2) + 16 * (gg % 2) + 8 * (P % 2) + 4 * (gg / 2);
+    float* dst = y + (unit * T + t0 + sn) * V + col;
+    if (atomic_y) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, sum[i]);
+    } else {
+      *reinterpret_cast<f4*>(dst) = sum;
+    }
+  };
+
+  // Chunk end: Dr holds the readouts of the chunk's steps t0 .. t0 + nsteps - 1.
+  // Publish the waves' partials, stage chunk c2 and fetch chunk c2 + 1, sum the
+  // partials into y. Two LDS barriers: the first publishes the partials, the
+  // second keeps the next chunk end's partials from overwriting them before every
+  // wave has summed, and publishes the staged chunk before the step that first
+  // prefetches from it.
+  auto chunk_end = [&](int t0, int nsteps, int c2) {
     float* ypw = yp_all + w * kChunk * V;
 #pragma unroll
     for (int P = 0; P < CT; ++P) *reinterpret_cast<f4*>(ypw + n * V + 16 * P + 4 * g) = Dr[P];
 #pragma unroll
     for (int P = 0; P < CT; ++P) Dr[P] = f4{0, 0, 0, 0};
-    __syncthreads();
-    // groups of 4 positions: (step, position/4)
-    for (int grp = tid; grp < nsteps * (V / 4); grp += L::THREADS) {
-      const int sn = grp / (V / 4), pos = 4 * (grp % (V / 4));
-      f4 sum = *reinterpret_cast<const f4*>(yp_all + sn * V + pos);
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(yp_all + (ww * kChunk + sn) * V + pos);
-      sum *= kInvC;
-      // position 16 P + 4 gg  ->  column 32 (P/2) + 16 (gg%2) + 8 (P%2) + 4 (gg/2)
-      const int P = pos / 16, gg = (pos % 16) / 4;
-      const int col = 32 * (P / 2) + 16 * (gg % 2) + 8 * (P % 2) + 4 * (gg / 2);
-      float* dst = y + (unit * T + t0 + sn) * V + col;
-      if (atomic_y) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, sum[i]);
-      } else {
-        *reinterpret_cast<f4*>(dst) = sum;
-      }
-    }
-    const int c2 = tt / kChunk + 2;  // chunk after next
+    lds_barrier();
+    // stage before the atomics go out: the registers being stored were loaded
+    // a whole chunk ago, and waiting for them does not wait for the atomics
     if (c2 < nchunks) {
       st.store(lds, c2 % NSB);
       if (c2 + 1 < nchunks) st.load(a, unit, row0, c2 + 1);
     }
-    __syncthreads();
+    if (nsteps == kChunk) {
+      constexpr int NG = kChunk * (V / 4) / L::THREADS;
+      static_assert(NG * L::THREADS == kChunk * (V / 4), "whole groups per thread");
+#pragma unroll
+      for (int i = 0; i < NG; ++i) ysum_group(t0, tid + i * L::THREADS);
+    } else {
+      for (int grp = tid; grp < nsteps * (V / 4); grp += L::THREADS) ysum_group(t0, grp);
+    }
+    lds_barrier();
   };
 
   // epilogue of state tiles 2b, 2b+1: tanh via exp2/rcp, gate blend, next operand
@@ -473,12 +496,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int b = 1; b < KB; ++b) {
       products(b - 1, 0, CT, nxt);
-      if (b == 1 && even) readout(t >= 2 ? t - 2 : 0, s >= 2, s >= 2);
+      if (b == 1 && even) readout(t >= 2 ? t - 2 : 0, t >= 2, t >= 2);
       epilogue(b, cur, fg, av, m2a, hdst);
       __builtin_amdgcn_sched_barrier(0);
     }
     products(KB - 1, 0, 2, nxt);
-    if (s == kChunk - 1 || t == T - 1) chunk_end(t);
+    // the readout above has just completed the previous chunk
+    if (s == 0 && t > 0) chunk_end(t - kChunk, kChunk, t / kChunk + 1);
   };
 
   // prologue: c (H_0 W + k_0 v_0^T) for step 0, last operand block for tiles 0, 1 only
@@ -495,6 +519,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     step(t + 1, accB, accA, false, pre);
   }
   if (t < T) step(t, accA, accB, true, pre);
+  // the steps not yet read out (the last one or two) and the last chunk's y
+  {
+    const int te = (T - 1) & ~1;
+    readout(te, true, te + 1 < T);
+    const int t0 = (T - 1) - (T - 1) % kChunk;
+    chunk_end(t0, T - t0, nchunks);
+  }
 
   if (a.HT) {
     float* HT = a.HT + (unit * a.K + my_row) * V;
