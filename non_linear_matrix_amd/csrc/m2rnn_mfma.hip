@@ -148,7 +148,9 @@ struct Stager {
         if (t < a.T) reg[p] = *reinterpret_cast<const u4*>(v + (unit * a.T + t) * V + 8 * part);
       }
     }
-    freg = 0;
+    // steps past T (the tail of the last chunk) get gate 1: they leave the state
+    // exactly unchanged, and their readouts are never stored
+    freg = 0x3f80u;
     if (tid < kChunk && t0 + tid < a.T) freg = f[unit * a.T + t0 + tid];
   }
 
@@ -234,6 +236,23 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// Issue order for one pipeline phase: each matrix instruction followed by NV
+// vector-ALU instructions, so the matrix core works while the wave issues the
+// epilogue (a wave issues in order: back-to-back MFMAs leave the VALU idle).
+template <int NM, int NV>
+__device__ __forceinline__ void interleave_mfma() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // NV VALU
+  }
+}
+// VALU instructions after each MFMA (measured on C3: phase 0 has 14 MFMAs, the
+// readout phase 16, the others 8, against ~44 VALU of epilogue each)
+constexpr int kNvPhase0 = 3, kNvReadout = 2, kNvPhase = 5;
+// the same for the two-pass variant (twice the product MFMAs)
+constexpr int kNvPhase0Split = 1, kNvReadoutSplit = 0, kNvPhaseSplit = 3;
 
 __device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -324,20 +343,28 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   if (nchunks > 2) st.load(a, unit, row0, 2);
   __syncthreads();
 
-  auto sbuf = [](int tt) { return (tt / kChunk) % NSB; };
+  // one stage buffer's views
+  struct Buf {
+    const unsigned int* kx;
+    const unsigned int* vx;
+    const unsigned short* qs;
+    const float* fs;
+  };
+  auto buf = [&](int sb) {
+    return Buf{kx_all + sb * kChunk * R, vx_all + sb * kChunk * 16 * NVX, qs_all + sb * kChunk * R,
+               fs_all + sb * kChunk * 4};
+  };
 
-  // rank-1 write of step tt as the initial accumulator: acc[c] = (v_tt, tile c) x (hi, lo of c k_tt).
-  // Operands are fetched one step ahead (R1 holds them in registers).
+  // rank-1 write of a step as the initial accumulator: acc[c] = (v, tile c) x (hi, lo of c k).
   struct R1 {
     unsigned int kpair;
     u4 win[CT / 2];  // window k: packed pairs 2k .. 2k+3 (tiles 2k, 2k+1 use dword 0 / 1)
   };
-  auto rank1_load = [&](int tt) {
+  auto rank1_load = [&](const Buf& B, int s) {
     R1 r;
-    const int s = tt % kChunk, sb = sbuf(tt);
-    const unsigned int* kp = (g == 0) ? kx_all + (sb * kChunk + s) * R + 16 * w + n : zero_lds;
+    const unsigned int* kp = (g == 0) ? B.kx + s * R + 16 * w + n : zero_lds;
     r.kpair = *kp;
-    const unsigned int* vp = vx_all + ((sb * kChunk + s) * 16 + n) * NVX;
+    const unsigned int* vp = B.vx + (s * 16 + n) * NVX;
 #pragma unroll
     for (int k = 0; k < CT / 2; ++k) {
       const uint2 lo = *reinterpret_cast<const uint2*>(vp + 2 * k);
@@ -361,19 +388,17 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int p = 0; p < CT; ++p) Dr[p] = f4{0, 0, 0, 0};
 
-  // readout of the step pair (tt0, tt0 + 1), tt0 even, state tiles in slots tt0 & 3
-  // and (tt0 + 1) & 3; a step contributes only where valid0 / valid1
-  auto readout = [&](int tt0, bool valid0, bool valid1) {
-    const int s0 = tt0 % kChunk, sb = sbuf(tt0);
+  // readout of the steps s0, s0 + 1 (s0 even) of the chunk in B, state tiles in
+  // slots s0 & 3 and (s0 + 1) & 3; contributes only if valid
+  auto readout = [&](const Buf& B, int s0, bool valid) {
     const int p = g / 2;                 // which step of the pair this lane group carries
     const int rr = 8 * (g % 2);          // first of its 8 rows
-    const int s = s0 + p;                // s0 even, so s <= kChunk - 1
-    s8 qv = *reinterpret_cast<const s8*>(qs_all + (sb * kChunk + s) * R + 16 * w + rr);
-    const bool valid = p ? valid1 : valid0;
+    const int s = s0 + p;
+    s8 qv = *reinterpret_cast<const s8*>(B.qs + s * R + 16 * w + rr);
     if (n != s || !valid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
     const bf16x8 Bq = __builtin_bit_cast(bf16x8, qv);
     // source lane (g, n): row rr + n/4 (+4) of the step's slot, positions 16 P + 4 (n % 4)
-    const unsigned short* src = hb_w + ((tt0 + p) & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
+    const unsigned short* src = hb_w + (s & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
 #pragma unroll
     for (int P = 0; P < CT; ++P) {
       const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * P));
@@ -460,71 +485,77 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // per-step operands fetched one step ahead: the gate scalars of step t and the
-  // rank-1 operands of step t + 1
+  // per-step operands fetched ahead: the gate scalars of the next step and the
+  // rank-1 operands of the step after it
   struct Pre {
     f4 fs;
     R1 r1;
   };
-  auto prefetch = [&](int t) {
-    Pre q;
-    const int tt = t < T ? t : T - 1;
-    q.fs = *reinterpret_cast<const f4*>(fs_all + (sbuf(tt) * kChunk + tt % kChunk) * 4);
-    // the two-pass variant has no registers to spare: it fetches at use instead
-    if constexpr (!SPLIT) q.r1 = rank1_load(t + 1 < T ? t + 1 : T - 1);
-    return q;
-  };
 
-  // One step. On entry `cur` holds c (G_{t-1} W + k_t v_t^T) except the last
-  // operand block's share for tiles 2.., which phase 0 adds. Step t+1's
+  // Step s of chunk c (C, Cn, Cp: the stage buffers of chunks c, c + 1, c - 1).
+  // On entry `cur` holds c (G_{t-1} W + k_t v_t^T) except the last operand
+  // block's share for tiles 2.., which phase 0 adds. The next step's
   // accumulators `nxt` start from its rank-1 write and take operand block b
   // right after the epilogue has produced it; block KB-1 is finished for tiles
   // 0, 1 here and for the other tiles in the next step's phase 0.
-  auto step = [&](int t, f4 (&cur)[CT], f4 (&nxt)[CT], bool even, Pre& pre) {
-    const int s = t % kChunk;
+  auto step = [&](const int s, f4 (&cur)[CT], f4 (&nxt)[CT], Pre& pre, const Buf& C, const Buf& Cn,
+                  const Buf& Cp, const int c) {
     const float fg = pre.fs[0], av = pre.fs[1], m2a = pre.fs[2];
-    unsigned short* hdst = hb_w + (t & (NHS - 1)) * 16 * HROW + n * HROW + 8 * g;
+    unsigned short* hdst = hb_w + (s & (NHS - 1)) * 16 * HROW + n * HROW + 8 * g;
     // phase 0
     products(KB - 1, 2, CT, cur);
-    if constexpr (SPLIT)
-      rank1_init(rank1_load(t + 1 < T ? t + 1 : t), nxt);
+    if constexpr (SPLIT)  // no registers to spare for the early fetch
+      rank1_init(s + 1 < kChunk ? rank1_load(C, s + 1) : rank1_load(Cn, s + 1 - kChunk), nxt);
     else
       rank1_init(pre.r1, nxt);
-    pre = prefetch(t + 1);
+    pre.fs = *reinterpret_cast<const f4*>(s + 1 < kChunk ? C.fs + (s + 1) * 4 : Cn.fs + (s + 1 - kChunk) * 4);
+    if constexpr (!SPLIT) pre.r1 = s + 2 < kChunk ? rank1_load(C, s + 2) : rank1_load(Cn, s + 2 - kChunk);
     epilogue(0, cur, fg, av, m2a, hdst);
+    interleave_mfma<(SPLIT ? 2 : 1) * (CT - 2) + CT, SPLIT ? kNvPhase0Split : kNvPhase0>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 1; b < KB; ++b) {
       products(b - 1, 0, CT, nxt);
-      if (b == 1 && even) readout(t >= 2 ? t - 2 : 0, t >= 2, t >= 2);
+      if (b == 1 && s % 2 == 0) {
+        // the previous two steps; at a chunk start they close the previous chunk
+        if (s >= 2) readout(C, s - 2, true);
+        else readout(Cp, kChunk - 2, c > 0);
+      }
       epilogue(b, cur, fg, av, m2a, hdst);
+      if (b == 1 && s % 2 == 0)
+        interleave_mfma<(SPLIT ? 2 : 1) * CT + CT, SPLIT ? kNvReadoutSplit : kNvReadout>();
+      else
+        interleave_mfma<(SPLIT ? 2 : 1) * CT, SPLIT ? kNvPhaseSplit : kNvPhase>();
       __builtin_amdgcn_sched_barrier(0);
     }
     products(KB - 1, 0, 2, nxt);
-    // the readout above has just completed the previous chunk
-    if (s == 0 && t > 0) chunk_end(t - kChunk, kChunk, t / kChunk + 1);
+    if (s == 0 && c > 0) chunk_end((c - 1) * kChunk, kChunk, c + 1);
   };
 
   // prologue: c (H_0 W + k_0 v_0^T) for step 0, last operand block for tiles 0, 1 only
   f4 accA[CT], accB[CT];
-  rank1_init(rank1_load(0), accA);
+  rank1_init(rank1_load(buf(0), 0), accA);
 #pragma unroll
   for (int b = 0; b < KB - 1; ++b) products(b, 0, CT, accA);
   products(KB - 1, 0, 2, accA);
+  Pre pre;
+  pre.fs = *reinterpret_cast<const f4*>(buf(0).fs);
+  if constexpr (!SPLIT) pre.r1 = rank1_load(buf(0), 1);
 
-  Pre pre = prefetch(0);
-  int t = 0;
-  for (; t + 1 < T; t += 2) {
-    step(t, accA, accB, true, pre);
-    step(t + 1, accB, accA, false, pre);
+  // Whole chunks; the tail steps of the last one are identity steps (gate 1).
+  for (int c = 0; c < nchunks; ++c) {
+    const Buf C = buf(c % NSB), Cn = buf((c + 1) % NSB), Cp = buf((c + NSB - 1) % NSB);
+#pragma unroll
+    for (int s = 0; s < kChunk; s += 2) {
+      step(s, accA, accB, pre, C, Cn, Cp, c);
+      step(s + 1, accB, accA, pre, C, Cn, Cp, c);
+    }
   }
-  if (t < T) step(t, accA, accB, true, pre);
-  // the steps not yet read out (the last one or two) and the last chunk's y
+  // the last chunk's final two steps and its y
   {
-    const int te = (T - 1) & ~1;
-    readout(te, true, te + 1 < T);
-    const int t0 = (T - 1) - (T - 1) % kChunk;
-    chunk_end(t0, T - t0, nchunks);
+    const int c = nchunks - 1;
+    readout(buf(c % NSB), kChunk - 2, true);
+    chunk_end(c * kChunk, T - c * kChunk, nchunks);
   }
 
   if (a.HT) {
