@@ -87,14 +87,20 @@ struct Layout {
   static constexpr int R = 16 * NW;   // rows per workgroup
   static constexpr int CT = V / 16;   // 16-column tiles
   static constexpr int KB = V / 32;   // 32-wide contraction blocks
-  static constexpr int NVX = (CT + 2 + 3) / 4 * 4;  // packed v pairs per lane per step (padded)
+  // dwords per row and step of the rank-1 A operands: per tile pair k, dwords
+  // 4k .. 4k+3 = (v pair of tile 2k, v pair of tile 2k+1, 0, 0), so one aligned
+  // 16-byte read is the operand; the 4 padding dwords make those reads
+  // conflict-free across a row group
+  static constexpr int NVX = 2 * CT + 4;
   static constexpr int HROW = V + 8;  // bf16 per LDS state row (padded)
-  static constexpr int NSB = 3;       // stage buffers: chunk c+1 is staged before chunk c ends
+  // stage buffers: chunk c+1 goes into chunk c-1's buffer early in chunk c, once
+  // the readout of chunk c-1's last steps (step 0 of chunk c) is behind a barrier
+  static constexpr int NSB = 2;
   static constexpr int NHS = 4;       // state-tile slots per wave (readout lags one step pair)
   static constexpr int THREADS = 64 * NW;
   // LDS regions (bytes)
   static constexpr int KX_BYTES = NSB * kChunk * R * 4;          // (hi, lo) of c k, bf16 pair
-  static constexpr int VX_BYTES = NSB * kChunk * 16 * NVX * 4;   // (v, v) bf16 pairs, [m][c]
+  static constexpr int VX_BYTES = NSB * kChunk * 16 * NVX * 4;   // rank-1 A operands, [s][m][.]
   static constexpr int QS_BYTES = NSB * kChunk * R * 2;          // q, bf16
   static constexpr int FS_BYTES = NSB * kChunk * 4 * 4;          // f, a, -2a, pad
   static constexpr int HB_BYTES = NW * NHS * 16 * HROW * 2;      // per-wave state tiles
@@ -193,7 +199,8 @@ struct Stager {
         for (int i = 0; i < 8; ++i) {
           const int col = 8 * part + i;
           const unsigned int raw = (r[i / 2] >> (16 * (i % 2))) & 0xffffu;
-          vx[(s * 16 + col % 16) * L::NVX + col / 16] = raw | (raw << 16);
+          const int tile = col / 16;
+          vx[(s * 16 + col % 16) * L::NVX + 4 * (tile / 2) + tile % 2] = raw | (raw << 16);
         }
       }
     }
@@ -252,7 +259,7 @@ __device__ __forceinline__ void interleave_mfma() {
 // readout phase 16, the others 8, against ~44 VALU of epilogue each)
 constexpr int kNvPhase0 = 3, kNvReadout = 2, kNvPhase = 5;
 // the same for the two-pass variant (twice the product MFMAs)
-constexpr int kNvPhase0Split = 1, kNvReadoutSplit = 0, kNvPhaseSplit = 3;
+constexpr int kNvPhase0Split = 1, kNvReadoutSplit = 1, kNvPhaseSplit = 3;
 
 __device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -282,10 +289,10 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   float* yp_all = reinterpret_cast<float*>(lds + L::YP_OFF);
   const unsigned int* zero_lds = reinterpret_cast<const unsigned int*>(lds + L::Z_OFF);
 
-  // ---- one-time LDS init: zero padding of the packed v pairs, the state tiles, the zero word
+  // ---- one-time LDS init: the zero dwords of the rank-1 operands, the state tiles, the zero word
   for (int i = tid; i < NSB * kChunk * 16; i += L::THREADS)
 #pragma unroll
-    for (int c = CT; c < NVX; ++c) vx_all[i * NVX + c] = 0u;
+    for (int k = 0; k < CT / 2; ++k) *reinterpret_cast<uint2*>(vx_all + i * NVX + 4 * k + 2) = uint2{0u, 0u};
   for (int i = tid; i < L::HB_BYTES / 4; i += L::THREADS)
     reinterpret_cast<unsigned int*>(lds + L::HB_OFF)[i] = 0u;
   if (tid < 4) reinterpret_cast<unsigned int*>(lds + L::Z_OFF)[tid] = 0u;
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   // rank-1 write of a step as the initial accumulator: acc[c] = (v, tile c) x (hi, lo of c k).
   struct R1 {
     unsigned int kpair;
-    u4 win[CT / 2];  // window k: packed pairs 2k .. 2k+3 (tiles 2k, 2k+1 use dword 0 / 1)
+    u4 win[CT / 2];  // tile pair k: (v pair of tile 2k, of tile 2k+1, 0, 0)
   };
   auto rank1_load = [&](const Buf& B, int s) {
     R1 r;
@@ -366,11 +373,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     r.kpair = *kp;
     const unsigned int* vp = B.vx + (s * 16 + n) * NVX;
 #pragma unroll
-    for (int k = 0; k < CT / 2; ++k) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(vp + 2 * k);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vp + 2 * k + 2);
-      r.win[k] = u4{lo.x, lo.y, hi.x, hi.y};
-    }
+    for (int k = 0; k < CT / 2; ++k) r.win[k] = *reinterpret_cast<const u4*>(vp + 4 * k);
     return r;
   };
   auto rank1_init = [&](const R1& r, f4 (&acc)[CT]) {
@@ -431,34 +434,39 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // Chunk end: Dr holds the readouts of the chunk's steps t0 .. t0 + nsteps - 1.
-  // Publish the waves' partials, stage chunk c2 and fetch chunk c2 + 1, sum the
-  // partials into y. Two LDS barriers: the first publishes the partials, the
-  // second keeps the next chunk end's partials from overwriting them before every
-  // wave has summed, and publishes the staged chunk before the step that first
-  // prefetches from it.
-  auto chunk_end = [&](int t0, int nsteps, int c2) {
+  // Chunk end, spread over the first steps of the next chunk so that its LDS
+  // round trips overlap with their compute:
+  //   step 0 (end): publish the waves' partial readouts of the finished chunk
+  //                 (Dr, which that step's readout has just completed); LDS barrier
+  //   step 1:       stage the next chunk from the registers loaded a chunk ago,
+  //                 then fetch the one after it
+  //   steps 2..:    sum the partials into y, one group per step and thread
+  //   step kSync:   LDS barrier: the staged chunk is visible before the step
+  //                 that first prefetches from it (step 14), and every wave has
+  //                 summed before the next chunk end overwrites the partials
+  constexpr int kGroups = kChunk * (V / 4) / L::THREADS;  // y-sum groups per thread
+  static_assert(kGroups * L::THREADS == kChunk * (V / 4), "whole groups per thread");
+  constexpr int kSync = 8;
+  static_assert(2 + kGroups <= kSync && kSync < kChunk - 2, "chunk-end schedule");
+  auto publish = [&]() {
     float* ypw = yp_all + w * kChunk * V;
 #pragma unroll
     for (int P = 0; P < CT; ++P) *reinterpret_cast<f4*>(ypw + n * V + 16 * P + 4 * g) = Dr[P];
 #pragma unroll
     for (int P = 0; P < CT; ++P) Dr[P] = f4{0, 0, 0, 0};
     lds_barrier();
-    // stage before the atomics go out: the registers being stored were loaded
-    // a whole chunk ago, and waiting for them does not wait for the atomics
-    if (c2 < nchunks) {
-      st.store(lds, c2 % NSB);
-      if (c2 + 1 < nchunks) st.load(a, unit, row0, c2 + 1);
+  };
+  auto stage_next = [&](int c1) {
+    if (c1 < nchunks) {
+      st.store(lds, c1 % NSB);
+      if (c1 + 1 < nchunks) st.load(a, unit, row0, c1 + 1);
     }
-    if (nsteps == kChunk) {
-      constexpr int NG = kChunk * (V / 4) / L::THREADS;
-      static_assert(NG * L::THREADS == kChunk * (V / 4), "whole groups per thread");
-#pragma unroll
-      for (int i = 0; i < NG; ++i) ysum_group(t0, tid + i * L::THREADS);
-    } else {
-      for (int grp = tid; grp < nsteps * (V / 4); grp += L::THREADS) ysum_group(t0, grp);
-    }
-    lds_barrier();
+  };
+  auto chunk_end_work = [&](int s, int c) {
+    if (s == 0) publish();
+    if (s == 1) stage_next(c + 1);
+    if (s >= 2 && s < 2 + kGroups) ysum_group((c - 1) * kChunk, tid + (s - 2) * L::THREADS);
+    if (s == kSync) lds_barrier();
   };
 
   // epilogue of state tiles 2b, 2b+1: tanh via exp2/rcp, gate blend, next operand
@@ -529,7 +537,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     products(KB - 1, 0, 2, nxt);
-    if (s == 0 && c > 0) chunk_end((c - 1) * kChunk, kChunk, c + 1);
+    if (c > 0) chunk_end_work(s, c);
   };
 
   // prologue: c (H_0 W + k_0 v_0^T) for step 0, last operand block for tiles 0, 1 only
@@ -555,7 +563,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   {
     const int c = nchunks - 1;
     readout(buf(c % NSB), kChunk - 2, true);
-    chunk_end(c * kChunk, T - c * kChunk, nchunks);
+    publish();
+    const int t0 = c * kChunk;
+    for (int grp = tid; grp < (T - t0) * (V / 4); grp += L::THREADS) ysum_group(t0, grp);
   }
 
   if (a.HT) {
