@@ -289,6 +289,36 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   float* yp_all = reinterpret_cast<float*>(lds + L::YP_OFF);
   const unsigned int* zero_lds = reinterpret_cast<const unsigned int*>(lds + L::Z_OFF);
 
+  // ---- W as permuted A fragments: Wf[c][b] lane (g,n) = W[32b + 16(j/4) + 4g + j%4][16c + n].
+  // The head's W goes through LDS (the state-tile region, not yet in use) with
+  // 16-byte loads, and each fragment comes back as two transposing reads.
+  bf16x8 Wf[CT][KB];
+  {
+    constexpr int WROW = HROW;  // padded row, as the state tiles
+    static_assert(V * WROW * 2 <= L::HB_BYTES, "W fits in the state-tile region");
+    unsigned short* wst = reinterpret_cast<unsigned short*>(lds + L::HB_OFF);
+    const u4* Wg = reinterpret_cast<const u4*>(static_cast<const unsigned short*>(a.W) + (long long)h * V * V);
+    for (int i = tid; i < V * V / 8; i += L::THREADS)
+      *reinterpret_cast<u4*>(wst + (i / (V / 8)) * WROW + 8 * (i % (V / 8))) = Wg[i];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        // lane (g, n) points at row 32b + 4g + n/4, columns 16c + 4(n%4) ..+3; the
+        // transpose hands it column 16c + n of rows 32b + 4g .. +3 (and +16 .. +19)
+        const unsigned short* src = wst + (32 * b + 4 * g + n / 4) * WROW + 16 * c + 4 * (n % 4);
+        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)src);
+        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * WROW));
+        s8 wa = s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        // pin the fragment to the accumulation registers: it is only ever a
+        // matrix operand, and this leaves the arch VGPRs to the epilogue
+        asm volatile("" : "=a"(wa) : "0"(wa));
+        Wf[c][b] = __builtin_bit_cast(bf16x8, wa);
+      }
+    __syncthreads();  // every wave has its fragments before the region is cleared
+  }
+
   // ---- one-time LDS init: the zero dwords of the rank-1 operands, the state tiles, the zero word
   for (int i = tid; i < NSB * kChunk * 16; i += L::THREADS)
 #pragma unroll
@@ -296,28 +326,6 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   for (int i = tid; i < L::HB_BYTES / 4; i += L::THREADS)
     reinterpret_cast<unsigned int*>(lds + L::HB_OFF)[i] = 0u;
   if (tid < 4) reinterpret_cast<unsigned int*>(lds + L::Z_OFF)[tid] = 0u;
-
-  // ---- W as permuted A fragments: Wf[c][b] lane (g,n) = W[32b + 16(j/4) + 4g + j%4][16c + n]
-  bf16x8 Wf[CT][KB];
-  {
-    const unsigned short* Wp = static_cast<const unsigned short*>(a.W) + (long long)h * V * V;
-#pragma unroll
-    for (int c = 0; c < CT; ++c)
-#pragma unroll
-      for (int b = 0; b < KB; ++b) {
-        u4 wa;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int row = 32 * b + 16 * (d / 2) + 4 * g + 2 * (d % 2);
-          wa[d] = static_cast<unsigned int>(Wp[row * V + 16 * c + n]) |
-                  (static_cast<unsigned int>(Wp[(row + 1) * V + 16 * c + n]) << 16);
-        }
-        // pin the fragment to the accumulation registers: it is only ever a
-        // matrix operand, and this leaves the arch VGPRs to the epilogue
-        asm volatile("" : "=a"(wa) : "0"(wa));
-        Wf[c][b] = __builtin_bit_cast(bf16x8, wa);
-      }
-  }
 
   // ---- scaled fp32 state G = c H, output layout
   f4 G[CT];
