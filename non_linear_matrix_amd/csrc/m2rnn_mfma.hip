@@ -289,17 +289,40 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   float* yp_all = reinterpret_cast<float*>(lds + L::YP_OFF);
   const unsigned int* zero_lds = reinterpret_cast<const unsigned int*>(lds + L::Z_OFF);
 
+  // ---- prologue. Every global read of the prologue (W, H0, chunks 0 and 1) is
+  // issued before the first wait, so their latencies overlap.
+  Stager<V, NW> st, st1;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  st.load(a, unit, row0, 0);
+  if (nchunks > 1) st1.load(a, unit, row0, 1);
+  constexpr int WLOADS = V * V / 8 / L::THREADS;  // 16-byte pieces of W per thread
+  static_assert(WLOADS * 8 * L::THREADS == V * V, "W splits evenly over the workgroup");
+  u4 wreg[WLOADS];
+  {
+    const u4* Wg = reinterpret_cast<const u4*>(static_cast<const unsigned short*>(a.W) + (long long)h * V * V);
+#pragma unroll
+    for (int p = 0; p < WLOADS; ++p) wreg[p] = Wg[tid + p * L::THREADS];
+  }
+  f4 h0v[CT];
+  {
+    const float* H0 = a.H0 ? a.H0 + (unit * a.K + my_row) * V : nullptr;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) h0v[c] = H0 ? *reinterpret_cast<const f4*>(H0 + 16 * c + 4 * g) : f4{0, 0, 0, 0};
+  }
+
   // ---- W as permuted A fragments: Wf[c][b] lane (g,n) = W[32b + 16(j/4) + 4g + j%4][16c + n].
-  // The head's W goes through LDS (the state-tile region, not yet in use) with
-  // 16-byte loads, and each fragment comes back as two transposing reads.
+  // The head's W goes through LDS (the state-tile region, not yet in use), and
+  // each fragment comes back as two transposing reads.
   bf16x8 Wf[CT][KB];
   {
     constexpr int WROW = HROW;  // padded row, as the state tiles
     static_assert(V * WROW * 2 <= L::HB_BYTES, "W fits in the state-tile region");
     unsigned short* wst = reinterpret_cast<unsigned short*>(lds + L::HB_OFF);
-    const u4* Wg = reinterpret_cast<const u4*>(static_cast<const unsigned short*>(a.W) + (long long)h * V * V);
-    for (int i = tid; i < V * V / 8; i += L::THREADS)
-      *reinterpret_cast<u4*>(wst + (i / (V / 8)) * WROW + 8 * (i % (V / 8))) = Wg[i];
+#pragma unroll
+    for (int p = 0; p < WLOADS; ++p) {
+      const int i = tid + p * L::THREADS;
+      *reinterpret_cast<u4*>(wst + (i / (V / 8)) * WROW + 8 * (i % (V / 8))) = wreg[p];
+    }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < CT; ++c)
@@ -316,47 +339,29 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
         asm volatile("" : "=a"(wa) : "0"(wa));
         Wf[c][b] = __builtin_bit_cast(bf16x8, wa);
       }
-    __syncthreads();  // every wave has its fragments before the region is cleared
+    lds_barrier();  // every wave has its fragments before the region is cleared
   }
 
-  // ---- one-time LDS init: the zero dwords of the rank-1 operands, the state tiles, the zero word
+  // ---- one-time LDS init: the zero dwords of the rank-1 operands, the state tiles,
+  // the zero word; then chunks 0 and 1 into the stage buffers (other addresses)
   for (int i = tid; i < NSB * kChunk * 16; i += L::THREADS)
 #pragma unroll
     for (int k = 0; k < CT / 2; ++k) *reinterpret_cast<uint2*>(vx_all + i * NVX + 4 * k + 2) = uint2{0u, 0u};
   for (int i = tid; i < L::HB_BYTES / 4; i += L::THREADS)
     reinterpret_cast<unsigned int*>(lds + L::HB_OFF)[i] = 0u;
   if (tid < 4) reinterpret_cast<unsigned int*>(lds + L::Z_OFF)[tid] = 0u;
+  st.store(lds, 0);
+  if (nchunks > 1) st1.store(lds, 1);
+  if (nchunks > 2) st.load(a, unit, row0, 2);  // staged early in chunk 1
 
   // ---- scaled fp32 state G = c H, output layout
   f4 G[CT];
-  {
-    const float* H0 = a.H0 ? a.H0 + (unit * a.K + my_row) * V : nullptr;
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      if (H0) {
-        const f4 x = *reinterpret_cast<const f4*>(H0 + 16 * c + 4 * g);
-        G[c] = x * kC;
-      } else {
-        G[c] = f4{0, 0, 0, 0};
-      }
-    }
-  }
+  for (int c = 0; c < CT; ++c) G[c] = h0v[c] * kC;
   bf16x8 Bf[KB], Bl[KB];
 #pragma unroll
   for (int b = 0; b < KB; ++b) make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
-
-  // ---- input staging: chunks 0 and 1 published, chunk 2 in flight
-  Stager<V, NW> st;
-  const int nchunks = (T + kChunk - 1) / kChunk;
-  st.load(a, unit, row0, 0);
-  __syncthreads();  // LDS init done before the staging writes
-  st.store(lds, 0);
-  if (nchunks > 1) {
-    st.load(a, unit, row0, 1);
-    st.store(lds, 1);
-  }
-  if (nchunks > 2) st.load(a, unit, row0, 2);
-  __syncthreads();
+  lds_barrier();  // staged chunks and zeroed tiles visible; the chunk-2 loads stay in flight
 
   // one stage buffer's views
   struct Buf {
