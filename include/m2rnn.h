@@ -110,6 +110,24 @@ m2rnn_status m2rnn_fwd_ex(const void* k, const void* v, const void* q, const voi
                           int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                           m2rnn_algo algo, unsigned flags, void* stream);
 
+/* Variable-length batch in the padded layout above (continuous decoding and
+ * ragged batches). Sequence b uses its first seq_len[b] steps: T is the longest
+ * length and the rows t >= seq_len[b] of k, v, q, f are not read. H_T[b] is the
+ * state after seq_len[b] steps (H0[b] unchanged for seq_len[b] = 0), and the y
+ * rows t >= seq_len[b] are set to zero (left untouched with
+ * M2RNN_FLAG_ACCUMULATE_Y). For serving with a state cache, call with T = 1 and
+ * H_T == H0 and give idle sequences length 0. The per-step arithmetic is that of
+ * m2rnn_fwd; the pages define only the recurrence, so this entry point is an
+ * interface of this library.
+ *   seq_len: device array of B int32, 4-byte aligned; NULL means every length
+ *            is T. The host cannot read device memory without synchronising, so
+ *            the kernels clamp each length into [0, T] instead of rejecting it.
+ * Errors as m2rnn_fwd_ex, plus INVALID_VALUE for a misaligned seq_len. */
+m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const void* f, const void* W,
+                              const float* H0, float* y, float* H_T, const int* seq_len,
+                              int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                              m2rnn_algo algo, unsigned flags, void* stream);
+
 /* Host-only argument check: returns exactly what m2rnn_fwd_algo would return
  * before launching, without touching the GPU. */
 m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const void* f, const void* W,
@@ -139,7 +157,7 @@ m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dt
 /* Static text for a status code ("unknown status" for other values). */
 const char* m2rnn_status_string(m2rnn_status status);
 
-/* Library ABI version: major * 10000 + minor * 100 + patch. */
+/* Library ABI version: major * 10000 + minor * 100 + patch (0.2.0 added m2rnn_fwd_varlen). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

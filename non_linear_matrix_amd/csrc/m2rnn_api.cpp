@@ -65,16 +65,17 @@ m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dty
   return M2RNN_ALGO_SIMPLE;
 }
 
-m2rnn_status m2rnn_fwd_ex(const void* k, const void* v, const void* q, const void* f,
-                          const void* W, const float* H0, float* y, float* H_T, int B, int H,
-                          int T, int K, int V, m2rnn_dtype in_dtype, m2rnn_algo algo,
-                          unsigned flags, void* stream) {
+m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const void* f,
+                              const void* W, const float* H0, float* y, float* H_T,
+                              const int* seq_len, int B, int H, int T, int K, int V,
+                              m2rnn_dtype in_dtype, m2rnn_algo algo, unsigned flags, void* stream) {
   m2rnn_status st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
+  if (seq_len && (reinterpret_cast<std::uintptr_t>(seq_len) & 3u) != 0) return M2RNN_ERROR_INVALID_VALUE;
   if ((flags & ~static_cast<unsigned>(M2RNN_FLAG_ACCUMULATE_Y)) != 0u) return M2RNN_ERROR_NOT_SUPPORTED;
   if (algo == M2RNN_ALGO_AUTO) algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
   m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype == M2RNN_DTYPE_BF16 ? 1 : 0,
-                   (flags & M2RNN_FLAG_ACCUMULATE_Y) ? 1 : 0};
+                   (flags & M2RNN_FLAG_ACCUMULATE_Y) ? 1 : 0, seq_len};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT)
@@ -82,6 +83,14 @@ m2rnn_status m2rnn_fwd_ex(const void* k, const void* v, const void* q, const voi
   else
     e = m2rnn::launch_simple(a, s);
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+}
+
+m2rnn_status m2rnn_fwd_ex(const void* k, const void* v, const void* q, const void* f,
+                          const void* W, const float* H0, float* y, float* H_T, int B, int H,
+                          int T, int K, int V, m2rnn_dtype in_dtype, m2rnn_algo algo,
+                          unsigned flags, void* stream) {
+  return m2rnn_fwd_varlen(k, v, q, f, W, H0, y, H_T, nullptr, B, H, T, K, V, in_dtype, algo, flags,
+                          stream);
 }
 
 m2rnn_status m2rnn_fwd_algo(const void* k, const void* v, const void* q, const void* f,
@@ -136,6 +145,6 @@ const char* m2rnn_status_string(m2rnn_status status) {
   }
 }
 
-int m2rnn_version(void) { return 100; }
+int m2rnn_version(void) { return 200; }
 
 }  // extern "C"

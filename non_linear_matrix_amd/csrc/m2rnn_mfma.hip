@@ -130,7 +130,8 @@ struct Stager {
   u4 reg[L::SLOTS_PER_THREAD];
   unsigned short freg;  // one gate value (threads < kChunk)
 
-  __device__ __forceinline__ void load(const FwdArgs& a, long long unit, int row0, int chunk) {
+  // chunk `chunk` of a sequence with Tb steps (the row stride is a.T)
+  __device__ __forceinline__ void load(const FwdArgs& a, long long unit, int row0, int chunk, int Tb) {
     const int tid = threadIdx.x;
     const int t0 = chunk * kChunk;
     const unsigned short* k = static_cast<const unsigned short*>(a.k);
@@ -146,18 +147,18 @@ struct Stager {
         const int s2 = isq ? slot - L::SLOT_K : slot;
         const int s = s2 / (L::R / 8), part = s2 % (L::R / 8);
         const int t = t0 + s;
-        if (t < a.T) reg[p] = *reinterpret_cast<const u4*>((isq ? q : k) + (unit * a.T + t) * a.K + row0 + 8 * part);
+        if (t < Tb) reg[p] = *reinterpret_cast<const u4*>((isq ? q : k) + (unit * a.T + t) * a.K + row0 + 8 * part);
       } else if (slot < L::SLOTS) {
         const int s2 = slot - L::SLOT_K - L::SLOT_Q;
         const int s = s2 / (V / 8), part = s2 % (V / 8);
         const int t = t0 + s;
-        if (t < a.T) reg[p] = *reinterpret_cast<const u4*>(v + (unit * a.T + t) * V + 8 * part);
+        if (t < Tb) reg[p] = *reinterpret_cast<const u4*>(v + (unit * a.T + t) * V + 8 * part);
       }
     }
-    // steps past T (the tail of the last chunk) get gate 1: they leave the state
-    // exactly unchanged, and their readouts are never stored
+    // steps past the sequence's end get gate 1: they leave the state exactly
+    // unchanged, and their readouts are never stored
     freg = 0x3f80u;
-    if (tid < kChunk && t0 + tid < a.T) freg = f[unit * a.T + t0 + tid];
+    if (tid < kChunk && t0 + tid < Tb) freg = f[unit * a.T + t0 + tid];
   }
 
   // Publish into stage buffer `buf`: c k as a bf16 (hi, lo) pair per row, v as
@@ -278,7 +279,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   const long long unit = blockIdx.x / splits;
   const int row0 = (blockIdx.x % splits) * R;
   const int h = static_cast<int>(unit % a.H);
-  const int T = a.T;
+  const int T = a.T;  // row stride of the per-step inputs and of y
+  // this sequence's length (all of T unless lengths are given)
+  const int Tb = a.lens ? min(max(a.lens[unit / a.H], 0), T) : T;
   const int my_row = row0 + 16 * w + n;  // state row this lane carries (within the unit)
 
   const unsigned int* kx_all = reinterpret_cast<const unsigned int*>(lds + L::KX_OFF);
@@ -292,9 +295,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   // ---- prologue. Every global read of the prologue (W, H0, chunks 0 and 1) is
   // issued before the first wait, so their latencies overlap.
   Stager<V, NW> st, st1;
-  const int nchunks = (T + kChunk - 1) / kChunk;
-  st.load(a, unit, row0, 0);
-  if (nchunks > 1) st1.load(a, unit, row0, 1);
+  const int nchunks = (Tb + kChunk - 1) / kChunk;
+  st.load(a, unit, row0, 0, Tb);
+  if (nchunks > 1) st1.load(a, unit, row0, 1, Tb);
   constexpr int WLOADS = V * V / 8 / L::THREADS;  // 16-byte pieces of W per thread
   static_assert(WLOADS * 8 * L::THREADS == V * V, "W splits evenly over the workgroup");
   u4 wreg[WLOADS];
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   if (tid < 4) reinterpret_cast<unsigned int*>(lds + L::Z_OFF)[tid] = 0u;
   st.store(lds, 0);
   if (nchunks > 1) st1.store(lds, 1);
-  if (nchunks > 2) st.load(a, unit, row0, 2);  // staged early in chunk 1
+  if (nchunks > 2) st.load(a, unit, row0, 2, Tb);  // staged early in chunk 1
 
   // ---- scaled fp32 state G = c H, output layout
   f4 G[CT];
@@ -405,13 +408,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   for (int p = 0; p < CT; ++p) Dr[p] = f4{0, 0, 0, 0};
 
   // readout of the steps s0, s0 + 1 (s0 even) of the chunk in B, state tiles in
-  // slots s0 & 3 and (s0 + 1) & 3; contributes only if valid
-  auto readout = [&](const Buf& B, int s0, bool valid) {
+  // slots s0 & 3 and (s0 + 1) & 3; step s0 + p contributes only if p < nvalid
+  auto readout = [&](const Buf& B, int s0, int nvalid) {
     const int p = g / 2;                 // which step of the pair this lane group carries
     const int rr = 8 * (g % 2);          // first of its 8 rows
     const int s = s0 + p;
     s8 qv = *reinterpret_cast<const s8*>(B.qs + s * R + 16 * w + rr);
-    if (n != s || !valid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (n != s || p >= nvalid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
     const bf16x8 Bq = __builtin_bit_cast(bf16x8, qv);
     // source lane (g, n): row rr + n/4 (+4) of the step's slot, positions 16 P + 4 (n % 4)
     const unsigned short* src = hb_w + (s & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   auto stage_next = [&](int c1) {
     if (c1 < nchunks) {
       st.store(lds, c1 % NSB);
-      if (c1 + 1 < nchunks) st.load(a, unit, row0, c1 + 1);
+      if (c1 + 1 < nchunks) st.load(a, unit, row0, c1 + 1, Tb);
     }
   };
   auto chunk_end_work = [&](int s, int c) {
@@ -539,8 +542,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
       products(b - 1, 0, CT, nxt);
       if (b == 1 && s % 2 == 0) {
         // the previous two steps; at a chunk start they close the previous chunk
-        if (s >= 2) readout(C, s - 2, true);
-        else readout(Cp, kChunk - 2, c > 0);
+        if (s >= 2) readout(C, s - 2, 2);
+        else readout(Cp, kChunk - 2, c > 0 ? 2 : 0);
       }
       epilogue(b, cur, fg, av, m2a, hdst);
       if (b == 1 && s % 2 == 0)
@@ -563,28 +566,46 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   pre.fs = *reinterpret_cast<const f4*>(buf(0).fs);
   if constexpr (!SPLIT) pre.r1 = rank1_load(buf(0), 1);
 
-  // Whole chunks; the tail steps of the last one are identity steps (gate 1).
+  // Chunks of 16 steps in pairs; the last chunk stops after the pair that holds
+  // the sequence's last step (the pair's second step may be an identity step).
   for (int c = 0; c < nchunks; ++c) {
     const Buf C = buf(c % NSB), Cn = buf((c + 1) % NSB), Cp = buf((c + NSB - 1) % NSB);
+    const int ns = c == nchunks - 1 ? Tb - c * kChunk : kChunk;  // real steps in this chunk
 #pragma unroll
     for (int s = 0; s < kChunk; s += 2) {
       step(s, accA, accB, pre, C, Cn, Cp, c);
       step(s + 1, accB, accA, pre, C, Cn, Cp, c);
+      if (s + 2 >= ns) break;
     }
   }
-  // the last chunk's final two steps and its y
-  {
+  // the last chunk's pending steps and its y
+  if (nchunks > 0) {
     const int c = nchunks - 1;
-    readout(buf(c % NSB), kChunk - 2, true);
+    const int ns = Tb - c * kChunk;
+    if (c > 0) {
+      // the previous chunk's y groups a short last chunk did not reach, before
+      // the partials are overwritten
+      const int done = min(max(((ns + 1) & ~1) - 2, 0), kGroups);
+      for (int i = done; i < kGroups; ++i) ysum_group((c - 1) * kChunk, tid + i * L::THREADS);
+      lds_barrier();
+    }
+    const int te = (ns - 1) & ~1;
+    readout(buf(c % NSB), te, min(ns - te, 2));
     publish();
     const int t0 = c * kChunk;
-    for (int grp = tid; grp < (T - t0) * (V / 4); grp += L::THREADS) ysum_group(t0, grp);
+    for (int grp = tid; grp < ns * (V / 4); grp += L::THREADS) ysum_group(t0, grp);
   }
 
   if (a.HT) {
     float* HT = a.HT + (unit * a.K + my_row) * V;
+    const float* H0 = a.H0 ? a.H0 + (unit * a.K + my_row) * V : nullptr;
 #pragma unroll
-    for (int c = 0; c < CT; ++c) *reinterpret_cast<f4*>(HT + 16 * c + 4 * g) = G[c] * kInvC;
+    for (int c = 0; c < CT; ++c) {
+      f4 x = G[c] * kInvC;
+      if (nchunks == 0)  // an empty sequence hands H0 back unchanged
+        x = H0 ? *reinterpret_cast<const f4*>(H0 + 16 * c + 4 * g) : f4{0, 0, 0, 0};
+      *reinterpret_cast<f4*>(HT + 16 * c + 4 * g) = x;
+    }
   }
 }
 
@@ -600,12 +621,10 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int splits = a.K / R;
   const long long grid = (long long)a.B * a.H * splits;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (splits > 1 && !a.accumulate) {
-    const long long ny = (long long)a.B * a.H * a.T * a.V;
-    long long blocks = (ny + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.y, ny);
-    hipError_t e = hipGetLastError();
+  // y starts at zero when two workgroups add into it, or when sequences end
+  // early (their remaining rows read as zero)
+  if ((splits > 1 || a.lens) && !a.accumulate) {
+    hipError_t e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, SPLIT>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
@@ -626,6 +645,14 @@ int lds_bytes(int nw) {
 }
 
 }  // namespace
+
+hipError_t fill_zero(float* p, long long n, hipStream_t stream) {
+  long long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 bool mfma_supports(int K, int V, int bf16) {
   if (!bf16) return false;

@@ -37,13 +37,15 @@ __global__ __launch_bounds__(kThreads) void simple_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const long long unit = blockIdx.x;  // b * H + h
   const int h = static_cast<int>(unit % a.H);
+  // this sequence's length; y rows past it are left to the launcher's fill
+  const int Tb = a.lens ? min(max(a.lens[unit / a.H], 0), T) : T;
 
   for (int e = tid; e < V * V; e += kThreads) Ws[e] = load_in(a.W, (long long)h * V * V + e, a.bf16);
   for (int e = tid; e < KV; e += kThreads) Hs[e] = a.H0 ? a.H0[unit * KV + e] : 0.0f;
 
   const long long seqK = unit * (long long)T * K;
   const long long seqV = unit * (long long)T * V;
-  for (int t = 0; t < T; ++t) {
+  for (int t = 0; t < Tb; ++t) {
     __syncthreads();  // previous readout finished with ks/qs/vs; W and H0 staged
     for (int e = tid; e < K; e += kThreads) {
       ks[e] = load_in(a.k, seqK + (long long)t * K + e, a.bf16);
@@ -95,6 +97,10 @@ Plan plan_simple(int B, int H, int K, int V) {
 
 hipError_t launch_simple(const FwdArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)plan_simple(a.B, a.H, a.K, a.V).lds_bytes;
+  if (a.lens && !a.accumulate) {  // rows past a sequence's length read as zero
+    hipError_t e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream);
+    if (e != hipSuccess) return e;
+  }
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(simple_fwd_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib.m2rnn_fwd_algo.restype = i
     lib.m2rnn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i, ctypes.c_uint, vp]
     lib.m2rnn_fwd_ex.restype = i
+    lib.m2rnn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i, i, ctypes.c_uint, vp]
+    lib.m2rnn_fwd_varlen.restype = i
     lib.m2rnn_check_args.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i]
     lib.m2rnn_check_args.restype = i
     lib.m2rnn_pick_algo.argtypes = [i, i, i, i, i, i]
@@ -107,13 +109,15 @@ def declared_functions() -> list:
     return sorted(set(re.findall(r"\b(m2rnn_\w+)\s*\(", text)))
 
 
-def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, algo: str = "auto", stream=None,
+def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, seq_len=None, algo: str = "auto", stream=None,
         want_state: bool = True, accumulate_y: bool = False) -> Tuple["object", Optional["object"]]:
     """Run the forward recurrence on torch device tensors.
 
     k, q [B,H,T,K]; v [B,H,T,V]; f [B,H,T]; W [H,V,V] — all torch.bfloat16 or all
     torch.float32; H0 [B,H,K,V] float32 or None. y / H_T may be given (float32,
     contiguous) to write into; otherwise they are allocated with torch.
+    seq_len: optional int32 device tensor [B] of per-sequence lengths
+    (m2rnn_fwd_varlen); H_T may then be H0 itself for in-place continuation.
     Returns (y, H_T) (H_T is None when want_state is False and none was given).
     accumulate_y adds the readout into the given y (M2RNN_FLAG_ACCUMULATE_Y).
     """
@@ -129,7 +133,7 @@ def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, algo: str = "auto", stream=
     for name, t in (("v", v), ("q", q), ("f", f), ("W", W)):
         if t.dtype != k.dtype:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {k.dtype}")
-    tensors = [k, v, q, f, W] + [t for t in (H0, y, H_T) if t is not None]
+    tensors = [k, v, q, f, W] + [t for t in (H0, y, H_T, seq_len) if t is not None]
     for t in tensors:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("all tensors must be contiguous device tensors")
@@ -141,6 +145,8 @@ def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, algo: str = "auto", stream=
         raise ValueError("inconsistent shapes")
     if H0 is not None and (H0.dtype != torch.float32 or tuple(H0.shape) != (B, H, K, V)):
         raise ValueError("H0 must be float32 [B,H,K,V]")
+    if seq_len is not None and (seq_len.dtype != torch.int32 or tuple(seq_len.shape) != (B,)):
+        raise ValueError("seq_len must be int32 [B]")
     if accumulate_y and y is None:
         raise ValueError("accumulate_y needs y")
     if y is None:
@@ -154,9 +160,9 @@ def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, algo: str = "auto", stream=
     if stream is None:
         stream = torch.cuda.current_stream(k.device)
     ptr = lambda t: None if t is None else t.data_ptr()
-    st = lib.m2rnn_fwd_ex(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(y), ptr(H_T),
-                          B, H, T, K, V, dt, ALGOS[algo], FLAG_ACCUMULATE_Y if accumulate_y else 0,
-                          stream.cuda_stream)
+    st = lib.m2rnn_fwd_varlen(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(y), ptr(H_T),
+                              ptr(seq_len), B, H, T, K, V, dt, ALGOS[algo],
+                              FLAG_ACCUMULATE_Y if accumulate_y else 0, stream.cuda_stream)
     if st != 0:
         raise M2RNNError(st, "m2rnn_fwd")
     return y, H_T

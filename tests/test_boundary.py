@@ -28,13 +28,13 @@ def _check(**over):
 def test_library_exists_and_loads():
     assert os.path.exists(m2rnn.LIB_PATH), "build the library first (python -m non_linear_matrix_amd.build)"
     lib = m2rnn.load()
-    assert m2rnn.version() == 100
+    assert m2rnn.version() == 200
 
 
 def test_every_declared_symbol_is_exported():
     names = m2rnn.declared_functions()
-    assert set(names) >= {"m2rnn_fwd", "m2rnn_fwd_algo", "m2rnn_check_args", "m2rnn_pick_algo",
-                          "m2rnn_status_string", "m2rnn_version"}
+    assert set(names) >= {"m2rnn_fwd", "m2rnn_fwd_algo", "m2rnn_fwd_ex", "m2rnn_fwd_varlen",
+                          "m2rnn_check_args", "m2rnn_pick_algo", "m2rnn_status_string", "m2rnn_version"}
     raw = ctypes.CDLL(m2rnn.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/m2rnn.h but not exported"
@@ -131,3 +131,14 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         m2rnn.fwd(x, x, x, torch.zeros((1, 1, 2), dtype=torch.bfloat16),
                   torch.zeros((1, 16, 16), dtype=torch.bfloat16))
+
+
+def test_varlen_rejects_a_misaligned_length_array():
+    lib = m2rnn.load()
+    p = 0x10000
+    st = lib.m2rnn_fwd_varlen(p, p, p, p, p, None, p, None, p + 2, 2, 2, 16, 64, 64,
+                              m2rnn.DTYPES["bf16"], m2rnn.ALGOS["mfma"], 0, None)
+    assert st == 1  # M2RNN_ERROR_INVALID_VALUE, before any HIP call
+    st = lib.m2rnn_fwd_varlen(None, p, p, p, p, None, p, None, p, 2, 2, 16, 64, 64,
+                              m2rnn.DTYPES["bf16"], m2rnn.ALGOS["mfma"], 0, None)
+    assert st == 1
