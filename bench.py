@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense matrix-core peaks
+HBM_PEAK_GBS = 8000.0                            # MI355X HBM3E
 METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 
 # HBM bytes per launch of the recurrence kernel: rocprofv3 --pmc FETCH_SIZE and
@@ -58,7 +59,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="C3")
+    ap.add_argument("--workload", default="C3",
+                    help="C1..C5 (the parity configurations), D1 (one decoding step, state in place) "
+                         "or R1 (C3's shape with ragged lengths)")
     ap.add_argument("--algo", default="mfma")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -128,7 +131,7 @@ def main():
     import torch
 
     from non_linear_matrix_amd import m2rnn
-    from non_linear_matrix_amd.inputs import CONFIGS, generate
+    from non_linear_matrix_amd.inputs import CONFIGS, SERVING, generate, ragged_lengths
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -137,7 +140,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     m2rnn.load()
-    cfg = CONFIGS[args.workload]
+    cfg = {**CONFIGS, **SERVING}[args.workload]
     plan = m2rnn.get_plan(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V, cfg.dtype, args.algo)
     print(f"[bench] workload {cfg} plan {plan}", file=sys.stderr, flush=True)
     x = generate(cfg, args.seed)
@@ -150,12 +153,17 @@ def main():
         else:
             dev[key] = torch.from_numpy(a).cuda()
     y = torch.zeros((cfg.B, cfg.H, cfg.T, cfg.V), dtype=torch.float32, device="cuda")
-    HT = torch.empty((cfg.B, cfg.H, cfg.K, cfg.V), dtype=torch.float32, device="cuda")
+    # D1 carries the state in place (H_T is H0), as a decoding loop does
+    HT = dev["H0"] if cfg.name == "D1" else torch.empty((cfg.B, cfg.H, cfg.K, cfg.V), dtype=torch.float32,
+                                                        device="cuda")
+    lens = ragged_lengths(cfg.B, cfg.T, args.seed) if cfg.name == "R1" else None
+    seq_len = None if lens is None else torch.from_numpy(lens).cuda()
     stream = torch.cuda.current_stream()
-    # When the kernel sums several workgroups' readouts into y, the step clears y
-    # itself (part of the timed work) and asks the library to accumulate, so the
-    # events below bracket the recurrence kernel alone.
-    clear_here = bool(plan["clears_y"])
+    # When the library would clear y first (several workgroups add into it, or
+    # sequences end early), the step clears y itself (part of the timed work) and
+    # asks the library to accumulate, so the events below bracket the recurrence
+    # kernel alone.
+    clear_here = bool(plan["clears_y"]) or lens is not None
 
     def step(ev0=None, ev1=None):
         if clear_here:
@@ -163,7 +171,7 @@ def main():
         if ev0 is not None:
             ev0.record(stream)
         m2rnn.fwd(dev["k"], dev["v"], dev["q"], dev["f"], dev["W"], dev["H0"], y=y, H_T=HT,
-                  algo=args.algo, stream=stream, accumulate_y=clear_here)
+                  seq_len=seq_len, algo=args.algo, stream=stream, accumulate_y=clear_here)
         if ev1 is not None:
             ev1.record(stream)
 
@@ -185,7 +193,7 @@ def main():
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_avg = sum(kern_ms) / len(kern_ms)
     ms_per_step = total_ms / args.steps
-    tokens = cfg.B * cfg.H * cfg.T
+    tokens = cfg.H * (int(lens.sum()) if lens is not None else cfg.B * cfg.T)
     value = tokens / (ms_per_step * 1e-3)
     flops = 2.0 * cfg.K * cfg.V * cfg.V * tokens          # H_{t-1} W per (b, h, t)
     esize = 2 if cfg.dtype == "bf16" else 4
@@ -193,8 +201,11 @@ def main():
     # H_T per unit; y per token (fp32)
     algo_bytes = (tokens * ((2 * cfg.K + cfg.V + 1) * esize + 4 * cfg.V) + cfg.H * cfg.V * cfg.V * esize
                   + 2 * cfg.B * cfg.H * cfg.K * cfg.V * 4)
-    achieved = flops / (kern_avg * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
+    # the bound is whichever of the matrix cores and HBM needs longer at its peak
+    hbm_bound = algo_bytes / (HBM_PEAK_GBS * 1e9) > flops / (peak * 1e12)
+    achieved = flops / (kern_avg * 1e-3) / 1e12
+    hbm_gbs = algo_bytes / (kern_avg * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": value,
@@ -210,18 +221,20 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} K={cfg.K} V={cfg.V} T={cfg.T}, "
-                        f"{cfg.dtype} inputs, fp32 state, seed {args.seed}",
+                        f"{cfg.dtype} inputs, fp32 state, seed {args.seed}"
+                        + (f", lengths U[{cfg.T // 4}, {cfg.T}] ({tokens // cfg.H} tokens)" if lens is not None else "")
+                        + (", state updated in place" if cfg.name == "D1" else ""),
             "B": cfg.B, "H": cfg.H, "K": cfg.K, "V": cfg.V, "T": cfg.T,
             "algo": plan["algo"], "grid": plan["grid"], "block": plan["block"],
             "parallelism": "one GPU; (b,h) units x row groups across CUs",
         },
         "mfma_util_pct": 100.0 * achieved / peak,
         "roofline": {
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": achieved / peak,
+            "bound": "hbm" if hbm_bound else "mfma",
+            "achieved": hbm_gbs if hbm_bound else achieved,
+            "peak": HBM_PEAK_GBS if hbm_bound else peak,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": hbm_gbs / HBM_PEAK_GBS if hbm_bound else achieved / peak,
             "traffic": measured_traffic(args.workload, plan["algo"]),
             "kernel": "mfma_fwd_kernel" if plan["algo"].startswith("mfma") else "simple_fwd_kernel",
             "kernel_avg_ms": kern_avg,

@@ -30,6 +30,8 @@ import numpy as np
 __all__ = [
     "Config",
     "CONFIGS",
+    "SERVING",
+    "ragged_lengths",
     "fp32_to_bf16_bits",
     "bf16_bits_to_fp32",
     "generate",
@@ -71,6 +73,22 @@ CONFIGS: Dict[str, Config] = {
     "C4": Config("C4", "bf16", 1, 32, 128, 128, 8192, "1", 2.0, "uniform"),
     "C5": Config("C5", "bf16", 2, 16, 64, 128, 32768, "rsqrtK", 3.0, "zero"),
 }
+
+
+# Serving-side workloads of the same recurrence, measured but not among the five
+# parity configurations: D1 is one decoding step (T = 1) for 512 sequences of 16
+# heads with the state carried in place; R1 is C3's shape as a ragged batch whose
+# lengths come from ``ragged_lengths``.
+SERVING: Dict[str, Config] = {
+    "D1": Config("D1", "bf16", 512, 16, 128, 128, 1, "1", 2.0, "uniform"),
+    "R1": Config("R1", "bf16", 8, 16, 128, 128, 2048, "1", 2.0, "uniform"),
+}
+
+
+def ragged_lengths(B: int, T: int, seed: int = 0) -> np.ndarray:
+    """Per-sequence lengths, uniform in [T/4, T], int32 (own generator stream)."""
+    rng = np.random.default_rng(seed + 1_000_003)
+    return rng.integers(max(T // 4, 1), T + 1, size=B).astype(np.int32)
 
 
 def fp32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
