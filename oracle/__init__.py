@@ -1,7 +1,8 @@
-"""fp64 CPU oracle for the M²RNN forward recurrence — test infrastructure only.
+"""fp64 CPU oracle for the M²RNN forward recurrence and its gradients — test infrastructure only.
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package. The product path (the HIP library and its binding) never
 does, and the two share no code.
 """
 from .m2rnn_ref import m2rnn_fwd_ref, round_to_bf16, widen  # noqa: F401
+from .m2rnn_bwd_ref import m2rnn_bwd_ref  # noqa: F401

@@ -41,6 +41,8 @@ def widen(x: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
         return None
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":  # exact fp64 inputs (finite-difference checks of the oracle)
+        return np.asarray(x, dtype=np.float64)
     if dtype == "bf16":
         u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(np.float32).astype(np.float64)
