@@ -128,6 +128,45 @@ m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const
                               int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                               m2rnn_algo algo, unsigned flags, void* stream);
 
+/* ---- Training: the forward pass that keeps what the backward pass reads, and
+ * the backward pass (gradients of a loss L given dL/dy and dL/dH_T). The
+ * gradients are the chain rule of the update equations above; the pages state
+ * that the backward pass works from recomputed forward states cached in HBM
+ * (zh summary §2.2, parallelism paragraph). Here the forward pass writes, per
+ * step, the bf16 state operand of the matrix product and the bf16
+ * pre-activation into `saved`, and the backward pass reads them in reverse.
+ * Both cover bf16 inputs on the MFMA kernel family only (K in {32, 64, 128},
+ * V in {64, 128}); other shapes and dtypes are NOT_SUPPORTED. */
+
+/* Bytes of the `saved` buffer for one forward pass of this shape
+ * ((2T + 1) * B * H * K * V * 2; 0 when the shape is not covered). */
+unsigned long long m2rnn_saved_bytes(int B, int H, int T, int K, int V);
+
+/* m2rnn_fwd_algo (algo AUTO, MFMA or MFMA_SPLIT) that also fills `saved`
+ * (device, 16-byte aligned, m2rnn_saved_bytes large, caller-owned; its layout
+ * is private to the library and only m2rnn_bwd reads it). */
+m2rnn_status m2rnn_fwd_save(const void* k, const void* v, const void* q, const void* f, const void* W,
+                            const float* H0, float* y, float* H_T, void* saved,
+                            int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, void* stream);
+
+/* Bytes of the backward pass's scratch buffer for this shape (0 when not covered). */
+unsigned long long m2rnn_bwd_workspace_bytes(int B, int H, int T, int K, int V);
+
+/* Backward pass. Inputs as m2rnn_fwd_save, plus `saved` from that call with the
+ * same inputs, dy [B][H][T][V] fp32 (dL/dy) and dH_T [B][H][K][V] fp32 (dL/dH_T;
+ * NULL means 0). Outputs, fp32 and caller-owned: dk, dq [B][H][T][K],
+ * dv [B][H][T][V], df [B][H][T], dW [H][V][V] (summed over the batch),
+ * dH0 [B][H][K][V] (may be NULL). `workspace`: device, 16-byte aligned,
+ * m2rnn_bwd_workspace_bytes large. The matrix products take the bf16 state and
+ * gradient operands, like the forward's MFMA kernel. Asynchronous on `stream`;
+ * the outputs are complete when the stream is. Errors as m2rnn_fwd_ex. */
+m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* f, const void* W,
+                       const float* H0, const void* saved, const float* dy, const float* dH_T,
+                       float* dk, float* dv, float* dq, float* df, float* dW, float* dH0,
+                       void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                       void* stream);
+
 /* Host-only argument check: returns exactly what m2rnn_fwd_algo would return
  * before launching, without touching the GPU. */
 m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const void* f, const void* W,

@@ -75,7 +75,7 @@ m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const
   if ((flags & ~static_cast<unsigned>(M2RNN_FLAG_ACCUMULATE_Y)) != 0u) return M2RNN_ERROR_NOT_SUPPORTED;
   if (algo == M2RNN_ALGO_AUTO) algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
   m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype == M2RNN_DTYPE_BF16 ? 1 : 0,
-                   (flags & M2RNN_FLAG_ACCUMULATE_Y) ? 1 : 0, seq_len};
+                   (flags & M2RNN_FLAG_ACCUMULATE_Y) ? 1 : 0, seq_len, nullptr};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT)
@@ -105,6 +105,47 @@ m2rnn_status m2rnn_fwd(const void* k, const void* v, const void* q, const void* 
                        m2rnn_dtype in_dtype, void* stream) {
   return m2rnn_fwd_algo(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, M2RNN_ALGO_AUTO,
                         stream);
+}
+
+unsigned long long m2rnn_saved_bytes(int B, int H, int T, int K, int V) {
+  if (B < 1 || H < 1 || T < 1 || !counts_fit(B, H, T, K, V) || !m2rnn::mfma_supports(K, V, 1)) return 0;
+  return static_cast<unsigned long long>(m2rnn::saved_total_bytes(B, H, T, K, V));
+}
+
+m2rnn_status m2rnn_fwd_save(const void* k, const void* v, const void* q, const void* f,
+                            const void* W, const float* H0, float* y, float* H_T, void* saved,
+                            int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, void* stream) {
+  if (algo == M2RNN_ALGO_AUTO) algo = M2RNN_ALGO_MFMA_SPLIT;
+  if (algo != M2RNN_ALGO_MFMA && algo != M2RNN_ALGO_MFMA_SPLIT) return M2RNN_ERROR_NOT_SUPPORTED;
+  m2rnn_status st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
+  if (st != M2RNN_SUCCESS) return st;
+  if (!saved || !aligned16(saved)) return M2RNN_ERROR_INVALID_VALUE;
+  m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, 1, 0, nullptr, saved};
+  hipError_t e = m2rnn::launch_mfma(a, algo == M2RNN_ALGO_MFMA_SPLIT, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+}
+
+unsigned long long m2rnn_bwd_workspace_bytes(int B, int H, int T, int K, int V) {
+  if (B < 1 || H < 1 || T < 1 || !counts_fit(B, H, T, K, V) || !m2rnn::mfma_supports(K, V, 1)) return 0;
+  return static_cast<unsigned long long>(m2rnn::bwd_workspace_bytes(B, H, T, K, V));
+}
+
+m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* f, const void* W,
+                       const float* H0, const void* saved, const float* dy, const float* dH_T,
+                       float* dk, float* dv, float* dq, float* df, float* dW, float* dH0,
+                       void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                       void* stream) {
+  // the forward's argument rules, with dy standing in for y
+  m2rnn_status st = check(k, v, q, f, W, H0, dy, dH_T, B, H, T, K, V, in_dtype, M2RNN_ALGO_MFMA);
+  if (st != M2RNN_SUCCESS) return st;
+  if (!saved || !dk || !dv || !dq || !df || !dW || !workspace) return M2RNN_ERROR_INVALID_VALUE;
+  if (!aligned16(saved) || !aligned16(dk) || !aligned16(dv) || !aligned16(dq) || !aligned16(df) ||
+      !aligned16(dW) || !aligned16(workspace) || (dH0 && !aligned16(dH0)))
+    return M2RNN_ERROR_INVALID_VALUE;
+  m2rnn::BwdLaunch p{k, v, q, f, W, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V};
+  hipError_t e = m2rnn::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
 }
 
 m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,

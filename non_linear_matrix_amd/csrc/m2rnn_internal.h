@@ -20,7 +20,25 @@ struct FwdArgs {
   int bf16;        // 1: inputs are bfloat16 bit patterns, 0: fp32
   int accumulate;  // 1: y += readout (y is never cleared by the library)
   const int* lens; // device [B] sequence lengths, clamped to [0, T]; null: all T
+  void* saved;     // training forward: per-step data for the backward pass; null: none
 };
+
+// Layout of the training forward's saved data (private to the library). A slot
+// holds one K x V matrix as bf16 in the MFMA register layout: K/16 row tiles x
+// V/32 blocks x 64 lanes x 16 bytes. Per unit there are T + 1 state slots (slot 0:
+// c H0, slot t + 1: c H_t, c = 2/ln 2, the operand of the next step's product),
+// and after all units' state slots, T pre-activation slots per unit (c A_t, as
+// the MFMA accumulators of tiles 2b, 2b + 1 packed per block b).
+__host__ __device__ inline long long saved_slot_bytes(int K, int V) { return (long long)K * V * 2; }
+__host__ __device__ inline long long saved_state_off(long long unit, int slot, int T, int K, int V) {
+  return (unit * (T + 1) + slot) * saved_slot_bytes(K, V);
+}
+__host__ __device__ inline long long saved_pre_off(long long unit, int t, int B, int H, int T, int K, int V) {
+  return ((long long)B * H * (T + 1) + unit * T + t) * saved_slot_bytes(K, V);
+}
+__host__ __device__ inline long long saved_total_bytes(int B, int H, int T, int K, int V) {
+  return (long long)B * H * (2LL * T + 1) * saved_slot_bytes(K, V);
+}
 
 // Launchers return the hipError_t of the launch (hipSuccess when enqueued).
 hipError_t launch_simple(const FwdArgs& a, hipStream_t stream);
@@ -31,6 +49,18 @@ hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream);
 bool mfma_supports(int K, int V, int bf16);
 // Fill n floats at p with zeros on `stream` (a kernel, so it can be captured).
 hipError_t fill_zero(float* p, long long n, hipStream_t stream);
+
+// Backward pass (bf16 inputs, MFMA shapes): the recurrence kernel, then dW.
+struct BwdLaunch {
+  const void *k, *v, *q, *f, *W;
+  const void* saved;
+  const float *dy, *dHT;
+  float *dk, *dv, *dq, *df, *dW, *dH0;
+  void* workspace;
+  int B, H, T, K, V;
+};
+hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream);
+long long bwd_workspace_bytes(int B, int H, int T, int K, int V);
 
 struct Plan {
   int grid, block, rows_per_group, groups_per_unit, clears_y, lds_bytes;

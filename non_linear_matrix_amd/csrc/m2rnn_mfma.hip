@@ -266,7 +266,7 @@ __device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int V, int NW, bool SPLIT>
+template <int V, int NW, bool SPLIT, bool SAVE>
 __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   using L = Layout<V, NW>;
   constexpr int R = L::R, CT = L::CT, KB = L::KB, HROW = L::HROW, NVX = L::NVX, NSB = L::NSB, NHS = L::NHS;
@@ -364,6 +364,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   bf16x8 Bf[KB], Bl[KB];
 #pragma unroll
   for (int b = 0; b < KB; ++b) make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
+  // training forward: this row tile's 16-byte piece of a saved slot, per block b
+  [[maybe_unused]] char* const saved = static_cast<char*>(a.saved);
+  [[maybe_unused]] const long long rt_off = (long long)(row0 / 16 + w) * (V / 32) * 1024 + l * 16;
+  if constexpr (SAVE) {
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+      *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, 0, T, a.K, V) + rt_off + b * 1024) = Bf[b];
+  }
   lds_barrier();  // staged chunks and zeroed tiles visible; the chunk-2 loads stay in flight
 
   // one stage buffer's views
@@ -487,7 +495,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 
   // epilogue of state tiles 2b, 2b+1: tanh via exp2/rcp, gate blend, next operand
   // block, rounded tile to the readout slot
-  auto epilogue = [&](int b, const f4 (&cur)[CT], float fg, float av, float m2a, unsigned short* hdst) {
+  auto epilogue = [&](int b, const f4 (&cur)[CT], float fg, float av, float m2a, unsigned short* hdst, int t) {
+    if constexpr (SAVE) {
+      // the pre-activation c A_t of tiles 2b, 2b+1, as bf16
+      if (t < T) {
+        const f4 u0 = cur[2 * b], u1 = cur[2 * b + 1];
+        const u4 pk = u4{pack_bf16(u0[0], u0[1]), pack_bf16(u0[2], u0[3]), pack_bf16(u1[0], u1[1]),
+                         pack_bf16(u1[2], u1[3])};
+        *reinterpret_cast<u4*>(saved + saved_pre_off(unit, t, a.B, a.H, T, a.K, V) + rt_off + b * 1024) = pk;
+      }
+    }
 #pragma unroll
     for (int c = 2 * b; c < 2 * b + 2; ++c) {
 #pragma unroll
@@ -499,6 +516,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     }
     make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
     *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
+    if constexpr (SAVE) {
+      if (t < T) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, t + 1, T, a.K, V) + rt_off + b * 1024) = Bf[b];
+    }
   };
 
   auto products = [&](int b, int c_lo, int c_hi, f4 (&acc)[CT]) {
@@ -534,7 +554,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
       rank1_init(pre.r1, nxt);
     pre.fs = *reinterpret_cast<const f4*>(s + 1 < kChunk ? C.fs + (s + 1) * 4 : Cn.fs + (s + 1 - kChunk) * 4);
     if constexpr (!SPLIT) pre.r1 = s + 2 < kChunk ? rank1_load(C, s + 2) : rank1_load(Cn, s + 2 - kChunk);
-    epilogue(0, cur, fg, av, m2a, hdst);
+    epilogue(0, cur, fg, av, m2a, hdst, c * kChunk + s);
     interleave_mfma<(SPLIT ? 2 : 1) * (CT - 2) + CT, SPLIT ? kNvPhase0Split : kNvPhase0>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -545,7 +565,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
         if (s >= 2) readout(C, s - 2, 2);
         else readout(Cp, kChunk - 2, c > 0 ? 2 : 0);
       }
-      epilogue(b, cur, fg, av, m2a, hdst);
+      epilogue(b, cur, fg, av, m2a, hdst, c * kChunk + s);
       if (b == 1 && s % 2 == 0)
         interleave_mfma<(SPLIT ? 2 : 1) * CT + CT, SPLIT ? kNvReadoutSplit : kNvReadout>();
       else
@@ -627,7 +647,10 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     hipError_t e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, SPLIT>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
+  if (a.saved)
+    hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, SPLIT, true>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, SPLIT, false>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "LIB_PATH", "M2RNNError", "load", "fwd", "check_args", "pick_algo", "status_string", "version",
+    "fwd_save", "bwd", "saved_bytes", "bwd_workspace_bytes",
     "STATUS", "ALGOS", "DTYPES", "declared_functions", "get_plan", "Plan", "FLAG_ACCUMULATE_Y",
 ]
 
@@ -74,6 +75,16 @@ def load() -> ctypes.CDLL:
     lib.m2rnn_status_string.restype = ctypes.c_char_p
     lib.m2rnn_get_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
     lib.m2rnn_get_plan.restype = i
+    u64 = ctypes.c_ulonglong
+    lib.m2rnn_saved_bytes.argtypes = [i, i, i, i, i]
+    lib.m2rnn_saved_bytes.restype = u64
+    lib.m2rnn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.m2rnn_bwd_workspace_bytes.restype = u64
+    lib.m2rnn_fwd_save.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i, i, vp]
+    lib.m2rnn_fwd_save.restype = i
+    lib.m2rnn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, vp,
+                              i, i, i, i, i, i, vp]
+    lib.m2rnn_bwd.restype = i
     lib.m2rnn_version.argtypes = []
     lib.m2rnn_version.restype = i
     _lib = lib
@@ -166,3 +177,74 @@ def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, seq_len=None, algo: str = "
     if st != 0:
         raise M2RNNError(st, "m2rnn_fwd")
     return y, H_T
+
+
+def saved_bytes(B: int, H: int, T: int, K: int, V: int) -> int:
+    """Size of the training forward's saved buffer (0: shape not covered)."""
+    return int(load().m2rnn_saved_bytes(B, H, T, K, V))
+
+
+def bwd_workspace_bytes(B: int, H: int, T: int, K: int, V: int) -> int:
+    return int(load().m2rnn_bwd_workspace_bytes(B, H, T, K, V))
+
+
+def fwd_save(k, v, q, f, W, H0=None, *, algo: str = "auto", stream=None):
+    """Training forward (m2rnn_fwd_save) on bf16 device tensors: returns
+    (y, H_T, saved), saved being the uint8 device buffer m2rnn_bwd reads."""
+    import torch
+
+    lib = load()
+    B, H, T, K = k.shape
+    V = v.shape[-1]
+    for t in [k, v, q, f, W] + ([H0] if H0 is not None else []):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    if k.dtype != torch.bfloat16:
+        raise TypeError("the training path takes bf16 inputs")
+    nbytes = saved_bytes(B, H, T, K, V)
+    if nbytes == 0:
+        raise M2RNNError(2, "m2rnn_saved_bytes")
+    saved = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
+    y = torch.empty((B, H, T, V), dtype=torch.float32, device=k.device)
+    HT = torch.empty((B, H, K, V), dtype=torch.float32, device=k.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(k.device)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.m2rnn_fwd_save(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(y), ptr(HT), ptr(saved),
+                            B, H, T, K, V, DTYPES["bf16"], ALGOS[algo], stream.cuda_stream)
+    if st != 0:
+        raise M2RNNError(st, "m2rnn_fwd_save")
+    return y, HT, saved
+
+
+def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, stream=None) -> dict:
+    """Backward pass (m2rnn_bwd): gradients dk, dv, dq, df, dW, dH0 (fp32)."""
+    import torch
+
+    lib = load()
+    B, H, T, K = k.shape
+    V = v.shape[-1]
+    dev = k.device
+    if dy.dtype != torch.float32 or tuple(dy.shape) != (B, H, T, V) or not dy.is_contiguous():
+        raise ValueError("dy must be contiguous float32 [B,H,T,V]")
+    if dH_T is not None and (dH_T.dtype != torch.float32 or tuple(dH_T.shape) != (B, H, K, V)):
+        raise ValueError("dH_T must be float32 [B,H,K,V]")
+    out = {
+        "dk": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
+        "dq": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
+        "dv": torch.empty((B, H, T, V), dtype=torch.float32, device=dev),
+        "df": torch.empty((B, H, T), dtype=torch.float32, device=dev),
+        "dW": torch.empty((H, V, V), dtype=torch.float32, device=dev),
+        "dH0": torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_dH0 else None,
+    }
+    ws = torch.empty(max(bwd_workspace_bytes(B, H, T, K, V), 16), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.m2rnn_bwd(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(saved), ptr(dy), ptr(dH_T),
+                       ptr(out["dk"]), ptr(out["dv"]), ptr(out["dq"]), ptr(out["df"]), ptr(out["dW"]),
+                       ptr(out["dH0"]), ptr(ws), B, H, T, K, V, DTYPES["bf16"], stream.cuda_stream)
+    if st != 0:
+        raise M2RNNError(st, "m2rnn_bwd")
+    out["workspace"] = ws  # keep alive until the stream has run
+    return out

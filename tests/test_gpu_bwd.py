@@ -1,0 +1,99 @@
+"""GPU parity of the training path (m2rnn_fwd_save + m2rnn_bwd) against the fp64
+gradient oracle on the same seeded inputs and output gradients.
+
+Metric as the forward tests: per gradient, max|g - g_ref| / max|g_ref|. The
+backward matrix products take bf16 operands (the saved state, dA), like the
+forward's MFMA kernel, so the bar is the bf16 one, 2e-2.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import announce, nerr, to_device
+from non_linear_matrix_amd.inputs import CONFIGS, generate, scaled
+from oracle import m2rnn_bwd_ref
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+GRADS = ("dk", "dv", "dq", "df", "dW", "dH0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from non_linear_matrix_amd import m2rnn
+    m2rnn.load()
+
+
+def _grads(cfg, seed, algo="auto", with_dHT=True):
+    import torch
+    from non_linear_matrix_amd import m2rnn
+
+    x = generate(cfg, seed)
+    rng = np.random.default_rng(seed + 77)
+    dy = rng.standard_normal((cfg.B, cfg.H, cfg.T, cfg.V)).astype(np.float32)
+    dHT = rng.standard_normal((cfg.B, cfg.H, cfg.K, cfg.V)).astype(np.float32) if with_dHT else None
+    d = to_device(x)
+    y, HT, saved = m2rnn.fwd_save(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], algo=algo)
+    g = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, torch.from_numpy(dy).cuda(),
+                  None if dHT is None else torch.from_numpy(dHT).cuda())
+    torch.cuda.synchronize()
+    got = {key: g[key].cpu().numpy() for key in GRADS}
+    got["y"], got["H_T"] = y.cpu().numpy(), HT.cpu().numpy()
+    ref = m2rnn_bwd_ref(x["k"], x["v"], x["q"], x["f"], x["W"], x["H0"], dy, dHT, dtype=cfg.dtype)
+    return got, ref
+
+
+SHAPES = [
+    ("C2", dict(B=2, H=2, T=20)),                    # K = V = 64, one workgroup per unit
+    ("C3", dict(B=1, H=2, T=37)),                    # K = V = 128, two workgroups, ragged T
+    ("C5", dict(B=2, H=1, T=16, K=32)),              # K = 32, V = 128, two-wave workgroups
+    ("C3", dict(B=2, H=2, T=48, K=64, V=128)),
+]
+
+
+@pytest.mark.parametrize("name,shape", SHAPES)
+def test_gradients_match_the_oracle(name, shape):
+    cfg = scaled(CONFIGS[name], **shape)
+    announce(f"bwd {name} {shape}")
+    got, ref = _grads(cfg, 31)
+    errs = {key: nerr(got[key], ref[key]) for key in GRADS}
+    errs["y"], errs["H_T"] = nerr(got["y"], ref["y"]), nerr(got["H_T"], ref["H_T"])
+    print(" ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for key, e in errs.items():
+        assert e <= TOL, f"{key}: {e:.3e}"
+
+
+def test_without_final_state_gradient():
+    cfg = scaled(CONFIGS["C2"], B=1, H=2, T=16)
+    announce("bwd without dH_T")
+    got, ref = _grads(cfg, 32, with_dHT=False)
+    for key in GRADS:
+        assert nerr(got[key], ref[key]) <= TOL, key
+
+
+def test_single_operand_forward_feeds_the_same_backward():
+    cfg = scaled(CONFIGS["C3"], B=1, H=2, T=24)
+    announce("bwd after the single-operand forward")
+    got, ref = _grads(cfg, 33, algo="mfma")
+    for key in GRADS:
+        assert nerr(got[key], ref[key]) <= TOL, key
+
+
+def test_backward_is_deterministic():
+    import torch
+    from non_linear_matrix_amd import m2rnn
+
+    cfg = scaled(CONFIGS["C3"], B=2, H=2, T=32)
+    announce("bwd determinism")
+    x = generate(cfg, 34)
+    d = to_device(x)
+    dy = torch.randn((cfg.B, cfg.H, cfg.T, cfg.V), generator=torch.Generator().manual_seed(5)).cuda()
+    _, _, saved = m2rnn.fwd_save(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"])
+    g1 = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, dy)
+    g2 = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, dy)
+    torch.cuda.synchronize()
+    for key in GRADS:
+        assert torch.equal(g1[key], g2[key]), key
