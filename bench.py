@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample (0 disables)")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training step instead: m2rnn_fwd_save then m2rnn_bwd (bf16 workloads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (a few times) and exit: "
                          "the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -120,6 +122,135 @@ def cpu_baseline(cfg, x, budget_s):
     }
 
 
+TRAIN_METRIC = "M2RNN training step (fwd_save + bwd) tokens·heads/sec at K=V=128, 1×MI355X"
+
+
+def cpu_baseline_train(cfg, x, dy, budget_s):
+    """The fp64 gradient oracle (forward included) on all units for a bounded
+    number of leading steps; tokens*heads/s of whole training steps."""
+    from oracle import m2rnn_bwd_ref
+
+    def run(ts):
+        sub = {k: (None if v is None else (v[:, :, :ts] if k in ("k", "v", "q", "f") else v)) for k, v in x.items()}
+        t0 = time.perf_counter()
+        m2rnn_bwd_ref(sub["k"], sub["v"], sub["q"], sub["f"], sub["W"], sub["H0"], dy[:, :, :ts], dtype=cfg.dtype)
+        return time.perf_counter() - t0
+
+    probe = min(4, cfg.T)
+    dt = run(probe)
+    # the oracle keeps every state and tanh output in fp64: at most 256 steps
+    ts = int(min(cfg.T, 256, max(probe, probe * budget_s / max(dt, 1e-6))))
+    dt = run(ts)
+    return {
+        "value": cfg.B * cfg.H * ts / dt,
+        "unit": "tok·heads/s",
+        "cores": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"fp64 numpy gradient oracle (forward + backward), all {cfg.B * cfg.H} (b,h) units of "
+                  f"{cfg.name}, first {ts} of {cfg.T} steps ({dt:.1f}s)",
+    }
+
+
+def train_bench(args, cfg, dev, x):
+    """Times whole training steps: the saving forward, then the backward pass
+    with output gradients dy (no gradient on the final state). The events bracket
+    each of the two calls on the launch stream."""
+    import numpy as np
+    import torch
+
+    from non_linear_matrix_amd import m2rnn
+
+    if cfg.dtype != "bf16":
+        print("the training path takes bf16 workloads", file=sys.stderr)
+        sys.exit(2)
+    B, H, T, K, V = cfg.B, cfg.H, cfg.T, cfg.K, cfg.V
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+    dy = torch.randn((B, H, T, V), dtype=torch.float32, device="cuda", generator=g)
+    y = torch.empty((B, H, T, V), dtype=torch.float32, device="cuda")
+    HT = torch.empty((B, H, K, V), dtype=torch.float32, device="cuda")
+    saved = torch.empty(m2rnn.saved_bytes(B, H, T, K, V), dtype=torch.uint8, device="cuda")
+    out = None
+    ws = torch.empty(max(m2rnn.bwd_workspace_bytes(B, H, T, K, V), 16), dtype=torch.uint8, device="cuda")
+    algo = args.algo if args.algo != "mfma" else "mfma_split"
+
+    def step(evs=None):
+        nonlocal out
+        if evs:
+            evs[0].record(stream)
+        m2rnn.fwd_save(dev["k"], dev["v"], dev["q"], dev["f"], dev["W"], dev["H0"], saved=saved, y=y, H_T=HT,
+                       algo=algo, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        out = m2rnn.bwd(dev["k"], dev["v"], dev["q"], dev["f"], dev["W"], dev["H0"], saved, dy, out=out,
+                        workspace=ws, stream=stream)
+        if evs:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    tokens = B * H * T
+    # algorithmic flops of the backward call: dA W^T (the state gradient) and
+    # H_{t-1}^T dA (the W gradient), 2 K V^2 each per (b, h, t)
+    bwd_flops = 4.0 * K * V * V * tokens
+    peak = PEAK_TFLOPS["bf16"]
+    achieved = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    saved_gb = saved.numel() / 1e9
+    res = {
+        "metric": TRAIN_METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tok·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={B} H={H} K={K} V={V} T={T}, {cfg.dtype} inputs, fp32 state, seed "
+                        f"{args.seed}; training step = m2rnn_fwd_save ({algo}) + m2rnn_bwd, dy ~ N(0,1)",
+            "B": B, "H": H, "K": K, "V": V, "T": T,
+            "parallelism": "one GPU; (b,h) units x row groups across CUs",
+        },
+        "fwd_save_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "saved_GB": saved_gb,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "kernel": "m2rnn_bwd call (mfma_bwd_kernel + dw_partial_kernel + dw_reduce_kernel)",
+            "kernel_avg_ms": bwd_ms,
+            "flops_per_launch": bwd_flops,
+        },
+        "wall_s": wall,
+    }
+    if args.cpu_seconds > 0:
+        dy_np = dy.cpu().numpy().astype(np.float64)
+        res["cpu_baseline"] = cpu_baseline_train(cfg, x, dy_np, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -152,6 +283,9 @@ def main():
             dev[key] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         else:
             dev[key] = torch.from_numpy(a).cuda()
+    if args.train:
+        train_bench(args, cfg, dev, x)
+        return
     y = torch.zeros((cfg.B, cfg.H, cfg.T, cfg.V), dtype=torch.float32, device="cuda")
     # D1 carries the state in place (H_T is H0), as a decoding loop does
     HT = dev["H0"] if cfg.name == "D1" else torch.empty((cfg.B, cfg.H, cfg.K, cfg.V), dtype=torch.float32,

@@ -188,9 +188,10 @@ def bwd_workspace_bytes(B: int, H: int, T: int, K: int, V: int) -> int:
     return int(load().m2rnn_bwd_workspace_bytes(B, H, T, K, V))
 
 
-def fwd_save(k, v, q, f, W, H0=None, *, algo: str = "auto", stream=None):
+def fwd_save(k, v, q, f, W, H0=None, *, saved=None, y=None, H_T=None, algo: str = "auto", stream=None):
     """Training forward (m2rnn_fwd_save) on bf16 device tensors: returns
-    (y, H_T, saved), saved being the uint8 device buffer m2rnn_bwd reads."""
+    (y, H_T, saved), saved being the uint8 device buffer m2rnn_bwd reads (pass
+    saved / y / H_T to reuse buffers)."""
     import torch
 
     lib = load()
@@ -204,9 +205,12 @@ def fwd_save(k, v, q, f, W, H0=None, *, algo: str = "auto", stream=None):
     nbytes = saved_bytes(B, H, T, K, V)
     if nbytes == 0:
         raise M2RNNError(2, "m2rnn_saved_bytes")
-    saved = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
-    y = torch.empty((B, H, T, V), dtype=torch.float32, device=k.device)
-    HT = torch.empty((B, H, K, V), dtype=torch.float32, device=k.device)
+    if saved is None:
+        saved = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
+    elif saved.numel() < nbytes or not saved.is_cuda:
+        raise ValueError(f"saved must be a device buffer of at least {nbytes} bytes")
+    y = torch.empty((B, H, T, V), dtype=torch.float32, device=k.device) if y is None else y
+    HT = torch.empty((B, H, K, V), dtype=torch.float32, device=k.device) if H_T is None else H_T
     if stream is None:
         stream = torch.cuda.current_stream(k.device)
     ptr = lambda t: None if t is None else t.data_ptr()
@@ -217,8 +221,10 @@ def fwd_save(k, v, q, f, W, H0=None, *, algo: str = "auto", stream=None):
     return y, HT, saved
 
 
-def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, stream=None) -> dict:
-    """Backward pass (m2rnn_bwd): gradients dk, dv, dq, df, dW, dH0 (fp32)."""
+def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, out=None, workspace=None,
+        stream=None) -> dict:
+    """Backward pass (m2rnn_bwd): gradients dk, dv, dq, df, dW, dH0 (fp32). `out`
+    (a dict as returned) and `workspace` may be passed to reuse buffers."""
     import torch
 
     lib = load()
@@ -229,15 +235,19 @@ def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, strea
         raise ValueError("dy must be contiguous float32 [B,H,T,V]")
     if dH_T is not None and (dH_T.dtype != torch.float32 or tuple(dH_T.shape) != (B, H, K, V)):
         raise ValueError("dH_T must be float32 [B,H,K,V]")
-    out = {
-        "dk": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
-        "dq": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
-        "dv": torch.empty((B, H, T, V), dtype=torch.float32, device=dev),
-        "df": torch.empty((B, H, T), dtype=torch.float32, device=dev),
-        "dW": torch.empty((H, V, V), dtype=torch.float32, device=dev),
-        "dH0": torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_dH0 else None,
-    }
-    ws = torch.empty(max(bwd_workspace_bytes(B, H, T, K, V), 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {
+            "dk": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
+            "dq": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
+            "dv": torch.empty((B, H, T, V), dtype=torch.float32, device=dev),
+            "df": torch.empty((B, H, T), dtype=torch.float32, device=dev),
+            "dW": torch.empty((H, V, V), dtype=torch.float32, device=dev),
+            "dH0": torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_dH0 else None,
+        }
+    need = max(bwd_workspace_bytes(B, H, T, K, V), 16)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    if ws.numel() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     ptr = lambda t: None if t is None else t.data_ptr()

@@ -97,3 +97,39 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for key in GRADS:
         assert torch.equal(g1[key], g2[key]), key
+
+
+FULL_HEADS = [("C3", 7), ("C4", 17), ("C5", 15)]
+
+
+@pytest.mark.parametrize("name,head", FULL_HEADS)
+def test_full_size_sampled_head(name, head):
+    """Full-size workloads in the launch configuration the training benchmark
+    uses; the oracle runs on every batch row of one head (dW of a head sums over
+    its batch rows, so a head is the smallest unit that checks every gradient)."""
+    import torch
+    from non_linear_matrix_amd import m2rnn
+
+    cfg = CONFIGS[name]
+    announce(f"bwd {name} full size, head {head}")
+    x = generate(cfg, 0)
+    rng = np.random.default_rng(99)
+    dy = rng.standard_normal((cfg.B, cfg.H, cfg.T, cfg.V), dtype=np.float32)
+    d = to_device(x)
+    y, HT, saved = m2rnn.fwd_save(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"])
+    g = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, torch.from_numpy(dy).cuda())
+    torch.cuda.synchronize()
+    got = {key: g[key][head].cpu().numpy() if key == "dW" else g[key][:, head].cpu().numpy() for key in GRADS}
+    del saved, g
+    sl = {key: (None if a is None else (a[head:head + 1] if key == "W" else a[:, head:head + 1]))
+          for key, a in x.items()}
+    ref = m2rnn_bwd_ref(sl["k"], sl["v"], sl["q"], sl["f"], sl["W"], sl["H0"], dy[:, head:head + 1],
+                        dtype=cfg.dtype)
+    errs = {}
+    for key in GRADS:
+        r = ref[key][0] if key == "dW" else ref[key][:, 0]
+        assert np.all(np.isfinite(got[key])), key
+        errs[key] = nerr(got[key], r)
+    print(f"{name} head {head}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for key, e in errs.items():
+        assert e <= TOL, f"{key}: {e:.3e}"
