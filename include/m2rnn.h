@@ -167,6 +167,48 @@ m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* 
                        void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                        void* stream);
 
+/* ---- Training with recomputation (zh summary §2.2, parallelism paragraph: the
+ * backward pass recomputes the forward states rather than keeping them all).
+ * The sequence is cut into segments of `segment` steps (the last one may be
+ * shorter). The training forward keeps only the state at each segment start
+ * after the first; the backward pass visits the segments last to first,
+ * recomputes each segment's states from its checkpoint into its workspace and
+ * runs the reverse-time pass over it. Memory: checkpoints of (ceil(T/segment) - 1)
+ * B H K V floats, plus a workspace that holds one segment. With segment >= T there
+ * is no checkpoint at all: the plain forward pass (m2rnn_fwd) is the training
+ * forward, and the backward pass recomputes the whole sequence from H0. Same
+ * shapes and dtypes as m2rnn_fwd_save; same outputs and errors as m2rnn_bwd. */
+
+/* Bytes of the checkpoint buffer: (ceil(T/segment) - 1) * B * H * K * V * 4
+ * (0: none needed, or invalid sizes). */
+unsigned long long m2rnn_ckpt_bytes(int B, int H, int T, int K, int V, int segment);
+
+/* m2rnn_fwd_algo (algo AUTO = MFMA_SPLIT, MFMA or MFMA_SPLIT) that also writes
+ * ckpt[j - 1] = H_{j * segment} for j = 1 .. ceil(T/segment) - 1, fp32
+ * [B][H][K][V] each (device, 16-byte aligned, caller-owned; may be NULL when
+ * m2rnn_ckpt_bytes is 0). It runs as one launch per segment.
+ * INVALID_VALUE also for segment < 1. */
+m2rnn_status m2rnn_fwd_ckpt(const void* k, const void* v, const void* q, const void* f, const void* W,
+                            const float* H0, float* y, float* H_T, float* ckpt,
+                            int B, int H, int T, int K, int V, int segment, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, void* stream);
+
+/* Bytes of m2rnn_bwd_recompute's workspace (0 when the shape is not covered). */
+unsigned long long m2rnn_bwd_recompute_workspace_bytes(int B, int H, int T, int K, int V, int segment);
+
+/* Backward pass from checkpoints: arguments as m2rnn_bwd, with `ckpt` from
+ * m2rnn_fwd_ckpt (same inputs, same segment) in place of `saved`, and H0 the
+ * initial state of the forward call (NULL: zero). `algo` (AUTO = MFMA_SPLIT)
+ * must be the one the forward pass ran, so that the recomputed states are the
+ * ones that produced y. `workspace`: m2rnn_bwd_recompute_workspace_bytes large.
+ * Issues five to seven launches per segment on `stream`. */
+m2rnn_status m2rnn_bwd_recompute(const void* k, const void* v, const void* q, const void* f,
+                                 const void* W, const float* H0, const float* ckpt, const float* dy,
+                                 const float* dH_T, float* dk, float* dv, float* dq, float* df,
+                                 float* dW, float* dH0, void* workspace, int B, int H, int T, int K,
+                                 int V, int segment, m2rnn_dtype in_dtype, m2rnn_algo algo,
+                                 void* stream);
+
 /* Host-only argument check: returns exactly what m2rnn_fwd_algo would return
  * before launching, without touching the GPU. */
 m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const void* f, const void* W,
@@ -196,7 +238,8 @@ m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dt
 /* Static text for a status code ("unknown status" for other values). */
 const char* m2rnn_status_string(m2rnn_status status);
 
-/* Library ABI version: major * 10000 + minor * 100 + patch (0.2.0 added m2rnn_fwd_varlen). */
+/* Library ABI version: major * 10000 + minor * 100 + patch (0.2.0 added
+ * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

@@ -148,6 +148,57 @@ m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* 
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
 }
 
+unsigned long long m2rnn_ckpt_bytes(int B, int H, int T, int K, int V, int segment) {
+  if (B < 1 || H < 1 || T < 1 || segment < 1 || !counts_fit(B, H, T, K, V)) return 0;
+  return static_cast<unsigned long long>(m2rnn::ckpt_bytes(B, H, T, K, V, segment));
+}
+
+m2rnn_status m2rnn_fwd_ckpt(const void* k, const void* v, const void* q, const void* f,
+                            const void* W, const float* H0, float* y, float* H_T, float* ckpt,
+                            int B, int H, int T, int K, int V, int segment, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, void* stream) {
+  if (algo == M2RNN_ALGO_AUTO) algo = M2RNN_ALGO_MFMA_SPLIT;
+  if (algo != M2RNN_ALGO_MFMA && algo != M2RNN_ALGO_MFMA_SPLIT) return M2RNN_ERROR_NOT_SUPPORTED;
+  m2rnn_status st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
+  if (st != M2RNN_SUCCESS) return st;
+  if (segment < 1) return M2RNN_ERROR_INVALID_VALUE;
+  if (m2rnn::ckpt_bytes(B, H, T, K, V, segment) > 0 && (!ckpt || !aligned16(ckpt)))
+    return M2RNN_ERROR_INVALID_VALUE;
+  m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, 1, 0, nullptr, nullptr, 0};
+  hipError_t e = m2rnn::launch_fwd_ckpt(a, ckpt, segment, algo == M2RNN_ALGO_MFMA_SPLIT,
+                                        reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+}
+
+unsigned long long m2rnn_bwd_recompute_workspace_bytes(int B, int H, int T, int K, int V, int segment) {
+  if (B < 1 || H < 1 || T < 1 || segment < 1 || !counts_fit(B, H, T, K, V) || !m2rnn::mfma_supports(K, V, 1))
+    return 0;
+  return static_cast<unsigned long long>(m2rnn::bwd_recompute_workspace_bytes(B, H, T, K, V, segment));
+}
+
+m2rnn_status m2rnn_bwd_recompute(const void* k, const void* v, const void* q, const void* f,
+                                 const void* W, const float* H0, const float* ckpt, const float* dy,
+                                 const float* dH_T, float* dk, float* dv, float* dq, float* df,
+                                 float* dW, float* dH0, void* workspace, int B, int H, int T, int K,
+                                 int V, int segment, m2rnn_dtype in_dtype, m2rnn_algo algo,
+                                 void* stream) {
+  if (algo == M2RNN_ALGO_AUTO) algo = M2RNN_ALGO_MFMA_SPLIT;
+  if (algo != M2RNN_ALGO_MFMA && algo != M2RNN_ALGO_MFMA_SPLIT) return M2RNN_ERROR_NOT_SUPPORTED;
+  m2rnn_status st = check(k, v, q, f, W, H0, dy, dH_T, B, H, T, K, V, in_dtype, algo);
+  if (st != M2RNN_SUCCESS) return st;
+  if (segment < 1 || !dk || !dv || !dq || !df || !dW || !workspace) return M2RNN_ERROR_INVALID_VALUE;
+  if (m2rnn::ckpt_bytes(B, H, T, K, V, segment) > 0 && (!ckpt || !aligned16(ckpt)))
+    return M2RNN_ERROR_INVALID_VALUE;
+  if (!aligned16(dk) || !aligned16(dv) || !aligned16(dq) || !aligned16(df) || !aligned16(dW) ||
+      !aligned16(workspace) || (dH0 && !aligned16(dH0)))
+    return M2RNN_ERROR_INVALID_VALUE;
+  m2rnn::BwdLaunch p{k, v, q, f, W, nullptr, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V,
+                     0, 0, 0};
+  hipError_t e = m2rnn::launch_bwd_recompute(p, H0, ckpt, segment, algo == M2RNN_ALGO_MFMA_SPLIT,
+                                             reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+}
+
 m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                             m2rnn_algo algo, m2rnn_plan* plan) {
   if (!plan) return M2RNN_ERROR_INVALID_VALUE;
@@ -186,6 +237,6 @@ const char* m2rnn_status_string(m2rnn_status status) {
   }
 }
 
-int m2rnn_version(void) { return 200; }
+int m2rnn_version(void) { return 300; }
 
 }  // extern "C"

@@ -103,6 +103,7 @@ struct BwdArgs {
   float *dk, *dv, *dq, *df, *dH0;
   char* dA_out;  // per-step bf16 dA, one saved-layout slot per (unit, t) (read by the dW kernel)
   int B, H, T, K;
+  long long ld;  // row stride (in steps) of the per-step inputs and gradients
 };
 
 // One chunk of per-step inputs, reversed: step s of chunk c is t = T - 1 - 16 c - s.
@@ -120,21 +121,21 @@ struct BwdStager {
       reg[p] = u4{0, 0, 0, 0};
       if (slot < L::SLOT_DY) {
         const int s = slot / (V / 4), part = slot % (V / 4), t = a.T - 1 - kChunk * c - s;
-        if (t >= 0) reg[p] = *reinterpret_cast<const u4*>(a.dy + (unit * a.T + t) * V + 4 * part);
+        if (t >= 0) reg[p] = *reinterpret_cast<const u4*>(a.dy + (unit * a.ld + t) * V + 4 * part);
       } else if ((slot -= L::SLOT_DY) < L::SLOT_V) {
         const int s = slot / (V / 8), part = slot % (V / 8), t = a.T - 1 - kChunk * c - s;
-        if (t >= 0) reg[p] = *reinterpret_cast<const u4*>(a.v + (unit * a.T + t) * V + 8 * part);
+        if (t >= 0) reg[p] = *reinterpret_cast<const u4*>(a.v + (unit * a.ld + t) * V + 8 * part);
       } else if ((slot -= L::SLOT_V) < L::SLOT_Q + L::SLOT_K) {
         const bool isk = slot >= L::SLOT_Q;
         const int s2 = isk ? slot - L::SLOT_Q : slot;
         const int s = s2 / (L::R / 8), part = s2 % (L::R / 8), t = a.T - 1 - kChunk * c - s;
-        if (t >= 0) reg[p] = *reinterpret_cast<const u4*>((isk ? a.k : a.q) + (unit * a.T + t) * a.K + row0 + 8 * part);
+        if (t >= 0) reg[p] = *reinterpret_cast<const u4*>((isk ? a.k : a.q) + (unit * a.ld + t) * a.K + row0 + 8 * part);
       }
     }
     // steps before t = 0 are inert: gate 1, zero inputs
     freg = 0x3f80u;
     const int t = a.T - 1 - kChunk * c - tid;
-    if (tid < kChunk && t >= 0) freg = a.f[unit * a.T + t];
+    if (tid < kChunk && t >= 0) freg = a.f[unit * a.ld + t];
   }
 
   __device__ __forceinline__ void store(char* lds, int buf) const {
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_bwd_kernel(BwdArgs a) {
       for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(yp_all + (ww * kChunk + sn) * V + pos);
       const int P = pos / 16, gg = (pos % 16) / 4;
       const int col = 32 * (P / 2) + 16 * (gg % 2) + 8 * (P % 2) + 4 * (gg / 2);
-      float* dst = a.dv + (unit * T + t) * V + col;
+      float* dst = a.dv + (unit * a.ld + t) * V + col;
       if (atomic) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, sum[i]);
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_bwd_kernel(BwdArgs a) {
       float sum = dfp_all[tid];
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) sum += dfp_all[ww * kChunk + tid];
-      float* dst = a.df + unit * T + (t_first - tid);
+      float* dst = a.df + unit * a.ld + (t_first - tid);
       if (atomic) unsafeAtomicAdd(dst, sum); else *dst = sum;
     }
     lds_barrier();
@@ -374,8 +375,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_bwd_kernel(BwdArgs a) {
       dkp += __shfl_xor(dkp, 16);
       dkp += __shfl_xor(dkp, 32);
       if (g == 0 && t >= 0) {
-        a.dq[(unit * T + t) * K + my_row] = dqp * kInvC;
-        a.dk[(unit * T + t) * K + my_row] = dkp;
+        a.dq[(unit * a.ld + t) * K + my_row] = dqp * kInvC;
+        a.dk[(unit * a.ld + t) * K + my_row] = dkp;
       }
       // df over the tile
 #pragma unroll
@@ -435,26 +436,44 @@ __global__ __launch_bounds__(256, 1) void dw_partial_kernel(const char* saved, c
 #pragma unroll
     for (int j = 0; j < CT; ++j) acc[i][j] = f4{0, 0, 0, 0};
 
-  for (long long blk = b0; blk < b1; ++blk) {
-    // block -> (batch row, step, row-tile pair)
-    const int pair = static_cast<int>(blk % (rtiles / 2));
+  // 2 matrices x 2 row tiles x V/32 blocks x 64 lanes of 16 bytes per block
+  constexpr int PIECES = 2 * 2 * (V / 32) * 64, PPT = PIECES / 256;
+  static_assert(PIECES % 256 == 0, "whole pieces per thread");
+  // global reads of one block into registers
+  auto fetch = [&](long long blk, u4 (&x)[PPT]) {
+    const int pair = static_cast<int>(blk % (rtiles / 2));  // block -> (batch row, step, row-tile pair)
     const long long bt = blk / (rtiles / 2);
     const int t = static_cast<int>(bt % T);
     const int bb = static_cast<int>(bt / T);
     const long long unit = (long long)bb * H + h;
     const char* srcs[2] = {saved + saved_state_off(unit, t, T, K, V), dA + (unit * T + t) * slot};
-    // 2 matrices x 2 row tiles x V/32 blocks x 64 lanes of 16 bytes
-    constexpr int PIECES = 2 * 2 * (V / 32) * 64;
-    for (int p = tid; p < PIECES; p += 256) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int p = tid + 256 * r;
+      const int m = p / (2 * (V / 32) * 64), q = p % (2 * (V / 32) * 64);
+      x[r] = *reinterpret_cast<const u4*>(srcs[m] + (long long)(2 * pair) * (V / 32) * 1024 + q * 16);
+    }
+  };
+  // the same pieces, row-major into LDS
+  auto put = [&](const u4 (&x)[PPT]) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int p = tid + 256 * r;
       const int m = p / (2 * (V / 32) * 64), q = p % (2 * (V / 32) * 64);
       const int rtl = q / ((V / 32) * 64), q2 = q % ((V / 32) * 64);
       const int bl = q2 / 64, lane = q2 % 64, lg = lane / 16, ln = lane % 16;
-      const u4 x = *reinterpret_cast<const u4*>(srcs[m] + (long long)(2 * pair + rtl) * (V / 32) * 1024 + bl * 1024 + lane * 16);
       unsigned short* row = tile[m] + (16 * rtl + ln) * HROW + 32 * bl + 4 * lg;
-      *reinterpret_cast<uint2*>(row) = uint2{x[0], x[1]};
-      *reinterpret_cast<uint2*>(row + 16) = uint2{x[2], x[3]};
+      *reinterpret_cast<uint2*>(row) = uint2{x[r][0], x[r][1]};
+      *reinterpret_cast<uint2*>(row + 16) = uint2{x[r][2], x[r][3]};
     }
+  };
+
+  u4 xr[PPT];
+  if (b0 < b1) fetch(b0, xr);
+  for (long long blk = b0; blk < b1; ++blk) {
+    put(xr);
     __syncthreads();
+    if (blk + 1 < b1) fetch(blk + 1, xr);  // in flight during this block's products
     // operands: rows 8g .. 8g+7 of the 32 at column base + n, two transposing reads each
     auto tr = [&](int m, int colbase) {
       const unsigned short* src = tile[m] + (8 * g + n / 4) * HROW + colbase + 4 * (n % 4);
@@ -483,32 +502,35 @@ __global__ __launch_bounds__(256, 1) void dw_partial_kernel(const char* saved, c
       for (int e = 0; e < 4; ++e) out[(16 * (LT * w + i) + 4 * g + e) * V + 16 * j + n] = acc[i][j][e];
 }
 
-__global__ void dw_reduce_kernel(const float* partial, float* dW, int H, int VV, int nsplit) {
+__global__ void dw_reduce_kernel(const float* partial, float* dW, int H, int VV, int nsplit, int accumulate) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long long)H * VV) return;
   const int h = static_cast<int>(i / VV), e = static_cast<int>(i % VV);
   const float* p = partial + (long long)h * nsplit * VV + e;
   float s = 0.0f;
   for (int k = 0; k < nsplit; ++k) s += p[(long long)k * VV];
-  dW[i] = s * kInvC;  // the saved operand is c H
+  s *= kInvC;  // the saved operand is c H
+  dW[i] = accumulate ? dW[i] + s : s;
 }
 
 int dw_splits(int B, int T, int K) {
   const long long blocks = (long long)B * T * (K / 32);
-  long long s = (blocks + 511) / 512;
+  long long s = (blocks + 127) / 128;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
   return static_cast<int>(s);
 }
 
 template <int V, int NW>
-hipError_t launch_bwd_t(const BwdArgs& a, float* partial, float* dW, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& a, float* partial, float* dW, bool zeroed, bool dW_acc,
+                        hipStream_t stream) {
   constexpr int R = 16 * NW;
   const int splits = a.K / R;
   const long long grid = (long long)a.B * a.H * splits;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipError_t e;
-  if (splits > 1) {  // dv and df take two workgroups' sums
+  if (splits > 1 && !zeroed) {  // dv and df take two workgroups' sums
+    if (a.ld != a.T) return hipErrorInvalidValue;  // a window: the caller clears dv and df
     if ((e = fill_zero(a.dv, (long long)a.B * a.H * a.T * V, stream)) != hipSuccess) return e;
     if ((e = fill_zero(a.df, (long long)a.B * a.H * a.T, stream)) != hipSuccess) return e;
   }
@@ -520,7 +542,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* partial, float* dW, hipStream_t
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long nel = (long long)a.H * V * V;
   hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, stream, partial, dW, a.H,
-                     V * V, ns);
+                     V * V, ns, dW_acc ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -534,12 +556,17 @@ hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream) {
   BwdArgs a{static_cast<const unsigned short*>(p.k), static_cast<const unsigned short*>(p.v),
             static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.f),
             static_cast<const unsigned short*>(p.W), static_cast<const char*>(p.saved), p.dy, p.dHT,
-            p.dk, p.dv, p.dq, p.df, p.dH0, static_cast<char*>(p.workspace), p.B, p.H, p.T, p.K};
+            p.dk, p.dv, p.dq, p.df, p.dH0, static_cast<char*>(p.workspace), p.B, p.H, p.T, p.K,
+            p.ld > 0 ? (long long)p.ld : (long long)p.T};
+  const bool z = p.dvdf_zeroed != 0, acc = p.dW_accumulate != 0;
   float* partial = reinterpret_cast<float*>(static_cast<char*>(p.workspace) +
                                             (long long)p.B * p.H * p.T * saved_slot_bytes(p.K, p.V));
   const int nw = p.K % 64 == 0 && p.K / 64 <= 2 ? 4 : (p.K % 32 == 0 && p.K / 32 <= 2 ? 2 : 0);
-  if (p.V == 128) return nw == 4 ? launch_bwd_t<128, 4>(a, partial, p.dW, stream) : launch_bwd_t<128, 2>(a, partial, p.dW, stream);
-  return nw == 4 ? launch_bwd_t<64, 4>(a, partial, p.dW, stream) : launch_bwd_t<64, 2>(a, partial, p.dW, stream);
+  if (p.V == 128)
+    return nw == 4 ? launch_bwd_t<128, 4>(a, partial, p.dW, z, acc, stream)
+                   : launch_bwd_t<128, 2>(a, partial, p.dW, z, acc, stream);
+  return nw == 4 ? launch_bwd_t<64, 4>(a, partial, p.dW, z, acc, stream)
+                 : launch_bwd_t<64, 2>(a, partial, p.dW, z, acc, stream);
 }
 
 }  // namespace m2rnn

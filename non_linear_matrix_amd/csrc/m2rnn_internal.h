@@ -21,7 +21,12 @@ struct FwdArgs {
   int accumulate;  // 1: y += readout (y is never cleared by the library)
   const int* lens; // device [B] sequence lengths, clamped to [0, T]; null: all T
   void* saved;     // training forward: per-step data for the backward pass; null: none
+  int ld;          // steps between consecutive units' rows of k, v, q, f and y (0: T), so
+                   // that a call can cover a window of a longer sequence; with ld != T
+                   // the library never clears y (accumulate, or y null)
 };
+// y may be null when `saved` is set: the states are recomputed for the backward
+// pass and the readout is not needed.
 
 // Layout of the training forward's saved data (private to the library). A slot
 // holds one K x V matrix as bf16 in the MFMA register layout: K/16 row tiles x
@@ -58,9 +63,22 @@ struct BwdLaunch {
   float *dk, *dv, *dq, *df, *dW, *dH0;
   void* workspace;
   int B, H, T, K, V;
+  int ld;             // steps between consecutive units' rows of k, v, q, f, dy, dk, dv, dq, df (0: T)
+  int dvdf_zeroed;    // 1: dv and df already hold zeros (the launcher does not clear them)
+  int dW_accumulate;  // 1: dW += this call's sum (else dW =)
 };
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream);
 long long bwd_workspace_bytes(int B, int H, int T, int K, int V);
+
+// Training with recomputation over segments of S steps (m2rnn_ckpt.cpp).
+long long ckpt_bytes(int B, int H, int T, int K, int V, int S);
+long long bwd_recompute_workspace_bytes(int B, int H, int T, int K, int V, int S);
+// a.saved, a.lens and a.ld are ignored; ckpt receives the states at steps S, 2S, ...
+hipError_t launch_fwd_ckpt(const FwdArgs& a, float* ckpt, int S, bool split, hipStream_t stream);
+// p.saved, p.ld and the flags are ignored; p.workspace holds
+// bwd_recompute_workspace_bytes; split picks the forward that recomputes the states
+hipError_t launch_bwd_recompute(const BwdLaunch& p, const float* H0, const float* ckpt, int S, bool split,
+                                hipStream_t stream);
 
 struct Plan {
   int grid, block, rows_per_group, groups_per_unit, clears_y, lds_bytes;

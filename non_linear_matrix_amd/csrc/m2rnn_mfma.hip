@@ -130,9 +130,10 @@ struct Stager {
   u4 reg[L::SLOTS_PER_THREAD];
   unsigned short freg;  // one gate value (threads < kChunk)
 
-  // chunk `chunk` of a sequence with Tb steps (the row stride is a.T)
+  // chunk `chunk` of a sequence with Tb steps (the row stride is ld)
   __device__ __forceinline__ void load(const FwdArgs& a, long long unit, int row0, int chunk, int Tb) {
     const int tid = threadIdx.x;
+    const long long ld = a.ld > 0 ? a.ld : a.T;
     const int t0 = chunk * kChunk;
     const unsigned short* k = static_cast<const unsigned short*>(a.k);
     const unsigned short* q = static_cast<const unsigned short*>(a.q);
@@ -147,18 +148,18 @@ struct Stager {
         const int s2 = isq ? slot - L::SLOT_K : slot;
         const int s = s2 / (L::R / 8), part = s2 % (L::R / 8);
         const int t = t0 + s;
-        if (t < Tb) reg[p] = *reinterpret_cast<const u4*>((isq ? q : k) + (unit * a.T + t) * a.K + row0 + 8 * part);
+        if (t < Tb) reg[p] = *reinterpret_cast<const u4*>((isq ? q : k) + (unit * ld + t) * a.K + row0 + 8 * part);
       } else if (slot < L::SLOTS) {
         const int s2 = slot - L::SLOT_K - L::SLOT_Q;
         const int s = s2 / (V / 8), part = s2 % (V / 8);
         const int t = t0 + s;
-        if (t < Tb) reg[p] = *reinterpret_cast<const u4*>(v + (unit * a.T + t) * V + 8 * part);
+        if (t < Tb) reg[p] = *reinterpret_cast<const u4*>(v + (unit * ld + t) * V + 8 * part);
       }
     }
     // steps past the sequence's end get gate 1: they leave the state exactly
     // unchanged, and their readouts are never stored
     freg = 0x3f80u;
-    if (tid < kChunk && t0 + tid < Tb) freg = f[unit * a.T + t0 + tid];
+    if (tid < kChunk && t0 + tid < Tb) freg = f[unit * ld + t0 + tid];
   }
 
   // Publish into stage buffer `buf`: c k as a bf16 (hi, lo) pair per row, v as
@@ -279,7 +280,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   const long long unit = blockIdx.x / splits;
   const int row0 = (blockIdx.x % splits) * R;
   const int h = static_cast<int>(unit % a.H);
-  const int T = a.T;  // row stride of the per-step inputs and of y
+  const int T = a.T;                                  // steps of this call
+  const long long LD = a.ld > 0 ? a.ld : a.T;          // row stride of the per-step inputs and of y
   // this sequence's length (all of T unless lengths are given)
   const int Tb = a.lens ? min(max(a.lens[unit / a.H], 0), T) : T;
   const int my_row = row0 + 16 * w + n;  // state row this lane carries (within the unit)
@@ -449,7 +451,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     // position 16 P + 4 gg  ->  column 32 (P/2) + 16 (gg%2) + 8 (P%2) + 4 (gg/2)
     const int P = pos / 16, gg = (pos % 16) / 4;
     const int col = 32 * (P / 2) + 16 * (gg % 2) + 8 * (P % 2) + 4 * (gg / 2);
-    float* dst = y + (unit * T + t0 + sn) * V + col;
+    if (y == nullptr) return;  // states recomputed for the backward pass: no readout wanted
+    float* dst = y + (unit * LD + t0 + sn) * V + col;
     if (atomic_y) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, sum[i]);
@@ -643,7 +646,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   // y starts at zero when two workgroups add into it, or when sequences end
   // early (their remaining rows read as zero)
-  if ((splits > 1 || a.lens) && !a.accumulate) {
+  if ((splits > 1 || a.lens) && !a.accumulate && a.y) {
+    if (a.ld > 0 && a.ld != a.T) return hipErrorInvalidValue;  // a window of y: the caller clears it
     hipError_t e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream);
     if (e != hipSuccess) return e;
   }

@@ -43,8 +43,9 @@ __global__ __launch_bounds__(kThreads) void simple_fwd_kernel(FwdArgs a) {
   for (int e = tid; e < V * V; e += kThreads) Ws[e] = load_in(a.W, (long long)h * V * V + e, a.bf16);
   for (int e = tid; e < KV; e += kThreads) Hs[e] = a.H0 ? a.H0[unit * KV + e] : 0.0f;
 
-  const long long seqK = unit * (long long)T * K;
-  const long long seqV = unit * (long long)T * V;
+  const long long ld = a.ld > 0 ? a.ld : T;  // row stride of the per-step arrays
+  const long long seqK = unit * ld * K;
+  const long long seqV = unit * ld * V;
   for (int t = 0; t < Tb; ++t) {
     __syncthreads();  // previous readout finished with ks/qs/vs; W and H0 staged
     for (int e = tid; e < K; e += kThreads) {
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void simple_fwd_kernel(FwdArgs a) {
       qs[e] = load_in(a.q, seqK + (long long)t * K + e, a.bf16);
     }
     for (int e = tid; e < V; e += kThreads) vs[e] = load_in(a.v, seqV + (long long)t * V + e, a.bf16);
-    if (tid == 0) fs[0] = load_in(a.f, unit * (long long)T + t, a.bf16);
+    if (tid == 0) fs[0] = load_in(a.f, unit * ld + t, a.bf16);
     __syncthreads();
     const float ft = fs[0];
     float nv[kMaxPerThread];
@@ -98,6 +99,7 @@ Plan plan_simple(int B, int H, int K, int V) {
 hipError_t launch_simple(const FwdArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)plan_simple(a.B, a.H, a.K, a.V).lds_bytes;
   if (a.lens && !a.accumulate) {  // rows past a sequence's length read as zero
+    if (a.ld > 0 && a.ld != a.T) return hipErrorInvalidValue;  // a window of y: the caller clears it
     hipError_t e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream);
     if (e != hipSuccess) return e;
   }

@@ -85,6 +85,15 @@ def load() -> ctypes.CDLL:
     lib.m2rnn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, vp,
                               i, i, i, i, i, i, vp]
     lib.m2rnn_bwd.restype = i
+    lib.m2rnn_ckpt_bytes.argtypes = [i, i, i, i, i, i]
+    lib.m2rnn_ckpt_bytes.restype = u64
+    lib.m2rnn_fwd_ckpt.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, i, i, i, vp]
+    lib.m2rnn_fwd_ckpt.restype = i
+    lib.m2rnn_bwd_recompute_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.m2rnn_bwd_recompute_workspace_bytes.restype = u64
+    lib.m2rnn_bwd_recompute.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, vp,
+                                        i, i, i, i, i, i, i, i, vp]
+    lib.m2rnn_bwd_recompute.restype = i
     lib.m2rnn_version.argtypes = []
     lib.m2rnn_version.restype = i
     _lib = lib
@@ -221,6 +230,29 @@ def fwd_save(k, v, q, f, W, H0=None, *, saved=None, y=None, H_T=None, algo: str 
     return y, HT, saved
 
 
+def _grad_buffers(B, H, T, K, V, dev, want_dH0):
+    import torch
+
+    return {
+        "dk": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
+        "dq": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
+        "dv": torch.empty((B, H, T, V), dtype=torch.float32, device=dev),
+        "df": torch.empty((B, H, T), dtype=torch.float32, device=dev),
+        "dW": torch.empty((H, V, V), dtype=torch.float32, device=dev),
+        "dH0": torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_dH0 else None,
+    }
+
+
+def _check_dy(dy, dH_T, B, H, T, K, V):
+    import torch
+
+    if dy.dtype != torch.float32 or tuple(dy.shape) != (B, H, T, V) or not dy.is_contiguous():
+        raise ValueError("dy must be contiguous float32 [B,H,T,V]")
+    if dH_T is not None and (dH_T.dtype != torch.float32 or tuple(dH_T.shape) != (B, H, K, V)
+                             or not dH_T.is_contiguous()):
+        raise ValueError("dH_T must be contiguous float32 [B,H,K,V]")
+
+
 def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, out=None, workspace=None,
         stream=None) -> dict:
     """Backward pass (m2rnn_bwd): gradients dk, dv, dq, df, dW, dH0 (fp32). `out`
@@ -231,19 +263,9 @@ def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, out=N
     B, H, T, K = k.shape
     V = v.shape[-1]
     dev = k.device
-    if dy.dtype != torch.float32 or tuple(dy.shape) != (B, H, T, V) or not dy.is_contiguous():
-        raise ValueError("dy must be contiguous float32 [B,H,T,V]")
-    if dH_T is not None and (dH_T.dtype != torch.float32 or tuple(dH_T.shape) != (B, H, K, V)):
-        raise ValueError("dH_T must be float32 [B,H,K,V]")
+    _check_dy(dy, dH_T, B, H, T, K, V)
     if out is None:
-        out = {
-            "dk": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
-            "dq": torch.empty((B, H, T, K), dtype=torch.float32, device=dev),
-            "dv": torch.empty((B, H, T, V), dtype=torch.float32, device=dev),
-            "df": torch.empty((B, H, T), dtype=torch.float32, device=dev),
-            "dW": torch.empty((H, V, V), dtype=torch.float32, device=dev),
-            "dH0": torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_dH0 else None,
-        }
+        out = _grad_buffers(B, H, T, K, V, dev, want_dH0)
     need = max(bwd_workspace_bytes(B, H, T, K, V), 16)
     ws = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else workspace
     if ws.numel() < need:
@@ -257,4 +279,79 @@ def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, out=N
     if st != 0:
         raise M2RNNError(st, "m2rnn_bwd")
     out["workspace"] = ws  # keep alive until the stream has run
+    return out
+
+
+def ckpt_bytes(B: int, H: int, T: int, K: int, V: int, segment: int) -> int:
+    """Size of the checkpoint buffer of m2rnn_fwd_ckpt (0: none needed)."""
+    return int(load().m2rnn_ckpt_bytes(B, H, T, K, V, segment))
+
+
+def bwd_recompute_workspace_bytes(B: int, H: int, T: int, K: int, V: int, segment: int) -> int:
+    return int(load().m2rnn_bwd_recompute_workspace_bytes(B, H, T, K, V, segment))
+
+
+def fwd_ckpt(k, v, q, f, W, H0=None, *, segment: int, ckpt=None, y=None, H_T=None, algo: str = "auto",
+             stream=None):
+    """Training forward with checkpoints every `segment` steps (m2rnn_fwd_ckpt) on
+    bf16 device tensors: returns (y, H_T, ckpt), ckpt a float32 device tensor
+    [nseg - 1, B, H, K, V] (None when there is a single segment)."""
+    import torch
+
+    lib = load()
+    B, H, T, K = k.shape
+    V = v.shape[-1]
+    for t in [k, v, q, f, W] + ([H0] if H0 is not None else []):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    if k.dtype != torch.bfloat16:
+        raise TypeError("the training path takes bf16 inputs")
+    nbytes = ckpt_bytes(B, H, T, K, V, segment)
+    if ckpt is None and nbytes > 0:
+        ckpt = torch.empty((nbytes // (4 * B * H * K * V), B, H, K, V), dtype=torch.float32, device=k.device)
+    if ckpt is not None and ckpt.numel() * 4 < nbytes:
+        raise ValueError(f"ckpt must hold {nbytes} bytes")
+    y = torch.empty((B, H, T, V), dtype=torch.float32, device=k.device) if y is None else y
+    HT = torch.empty((B, H, K, V), dtype=torch.float32, device=k.device) if H_T is None else H_T
+    if stream is None:
+        stream = torch.cuda.current_stream(k.device)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.m2rnn_fwd_ckpt(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(y), ptr(HT), ptr(ckpt),
+                            B, H, T, K, V, segment, DTYPES["bf16"], ALGOS[algo], stream.cuda_stream)
+    if st != 0:
+        raise M2RNNError(st, "m2rnn_fwd_ckpt")
+    return y, HT, ckpt
+
+
+def bwd_recompute(k, v, q, f, W, H0, ckpt, dy, dH_T=None, *, segment: int, algo: str = "auto",
+                  want_dH0: bool = True, out=None, workspace=None, stream=None) -> dict:
+    """Backward pass from checkpoints (m2rnn_bwd_recompute): recomputes each
+    segment's states, then its gradients. Returns the dict of bwd()."""
+    import torch
+
+    lib = load()
+    B, H, T, K = k.shape
+    V = v.shape[-1]
+    dev = k.device
+    _check_dy(dy, dH_T, B, H, T, K, V)
+    if ckpt_bytes(B, H, T, K, V, segment) > 0 and (ckpt is None or not ckpt.is_cuda):
+        raise ValueError("ckpt from fwd_ckpt is required for more than one segment")
+    if out is None:
+        out = _grad_buffers(B, H, T, K, V, dev, want_dH0)
+    need = bwd_recompute_workspace_bytes(B, H, T, K, V, segment)
+    if need == 0:
+        raise M2RNNError(2, "m2rnn_bwd_recompute_workspace_bytes")
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    if ws.numel() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.m2rnn_bwd_recompute(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(ckpt), ptr(dy), ptr(dH_T),
+                                 ptr(out["dk"]), ptr(out["dv"]), ptr(out["dq"]), ptr(out["df"]), ptr(out["dW"]),
+                                 ptr(out["dH0"]), ptr(ws), B, H, T, K, V, segment, DTYPES["bf16"], ALGOS[algo],
+                                 stream.cuda_stream)
+    if st != 0:
+        raise M2RNNError(st, "m2rnn_bwd_recompute")
+    out["workspace"] = ws
     return out

@@ -28,13 +28,16 @@ def _check(**over):
 def test_library_exists_and_loads():
     assert os.path.exists(m2rnn.LIB_PATH), "build the library first (python -m non_linear_matrix_amd.build)"
     lib = m2rnn.load()
-    assert m2rnn.version() == 200
+    assert m2rnn.version() == 300
 
 
 def test_every_declared_symbol_is_exported():
     names = m2rnn.declared_functions()
     assert set(names) >= {"m2rnn_fwd", "m2rnn_fwd_algo", "m2rnn_fwd_ex", "m2rnn_fwd_varlen",
-                          "m2rnn_check_args", "m2rnn_pick_algo", "m2rnn_status_string", "m2rnn_version"}
+                          "m2rnn_check_args", "m2rnn_pick_algo", "m2rnn_status_string", "m2rnn_version",
+                          "m2rnn_saved_bytes", "m2rnn_fwd_save", "m2rnn_bwd_workspace_bytes", "m2rnn_bwd",
+                          "m2rnn_ckpt_bytes", "m2rnn_fwd_ckpt", "m2rnn_bwd_recompute_workspace_bytes",
+                          "m2rnn_bwd_recompute"}
     raw = ctypes.CDLL(m2rnn.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/m2rnn.h but not exported"
@@ -142,3 +145,43 @@ def test_varlen_rejects_a_misaligned_length_array():
     st = lib.m2rnn_fwd_varlen(None, p, p, p, p, None, p, None, p, 2, 2, 16, 64, 64,
                               m2rnn.DTYPES["bf16"], m2rnn.ALGOS["mfma"], 0, None)
     assert st == 1
+
+
+def test_checkpoint_and_workspace_sizes():
+    B, H, T, K, V = 8, 16, 2048, 128, 128
+    kv = B * H * K * V * 4
+    assert m2rnn.ckpt_bytes(B, H, T, K, V, 256) == 7 * kv
+    assert m2rnn.ckpt_bytes(B, H, T, K, V, 300) == 6 * kv      # ceil(2048 / 300) = 7 segments
+    assert m2rnn.ckpt_bytes(B, H, T, K, V, T) == 0
+    assert m2rnn.ckpt_bytes(B, H, T, K, V, 10 * T) == 0
+    assert m2rnn.ckpt_bytes(B, H, T, K, V, 0) == 0
+    # one segment's saved data is what the workspace grows with
+    w256 = m2rnn.bwd_recompute_workspace_bytes(B, H, T, K, V, 256)
+    wall = m2rnn.bwd_recompute_workspace_bytes(B, H, T, K, V, T)
+    assert w256 >= m2rnn.saved_bytes(B, H, 256, K, V) + m2rnn.bwd_workspace_bytes(B, H, 256, K, V)
+    assert wall >= m2rnn.saved_bytes(B, H, T, K, V) + m2rnn.bwd_workspace_bytes(B, H, T, K, V)
+    assert w256 < wall / 6
+    assert m2rnn.bwd_recompute_workspace_bytes(B, H, T, K, V, 10 * T) == wall
+    assert m2rnn.bwd_recompute_workspace_bytes(B, H, T, 48, 112, 256) == 0   # not an MFMA shape
+
+
+def test_recompute_entry_points_validate_before_launching():
+    lib = m2rnn.load()
+    p = 0x10000
+    bf16, auto, simple = m2rnn.DTYPES["bf16"], m2rnn.ALGOS["auto"], m2rnn.ALGOS["simple"]
+    fwd = lambda ckpt, seg, algo=auto, dt=bf16: lib.m2rnn_fwd_ckpt(p, p, p, p, p, None, p, None, ckpt,
+                                                                   2, 2, 64, 64, 64, seg, dt, algo, None)
+    assert fwd(p, 0) == INVALID                 # segment < 1
+    assert fwd(None, 16) == INVALID             # four segments need checkpoints
+    assert fwd(p + 4, 16) == INVALID            # misaligned checkpoints
+    assert fwd(p, 16, algo=simple) == UNSUPPORTED
+    assert fwd(p, 16, dt=m2rnn.DTYPES["f32"]) == UNSUPPORTED
+
+    def bwd(ckpt, seg, ws=p, dk=p, algo=auto):
+        return lib.m2rnn_bwd_recompute(p, p, p, p, p, None, ckpt, p, None, dk, p, p, p, p, None, ws,
+                                       2, 2, 64, 64, 64, seg, bf16, algo, None)
+    assert bwd(p, 0) == INVALID
+    assert bwd(None, 16) == INVALID
+    assert bwd(p, 16, ws=None) == INVALID
+    assert bwd(p, 16, dk=None) == INVALID
+    assert bwd(p, 16, algo=simple) == UNSUPPORTED
