@@ -36,6 +36,9 @@ __all__ = [
     "bf16_bits_to_fp32",
     "generate",
     "scaled",
+    "frontend_width",
+    "frontend_rows",
+    "generate_frontend",
 ]
 
 
@@ -156,4 +159,41 @@ def generate(cfg: Config, seed: int = 0, *, qkv_scale: Optional[str] = None) -> 
         out["H0"] = None
     else:
         raise ValueError(f"unknown h0 {cfg.h0!r}")
+    return out
+
+
+# ---- inputs of the layer front-end (the projections of x_t that produce k, v,
+# q and the gate logit). The pages give no model width or weight scale; the
+# width is taken as D = H V (the layer's value width) and the weights are drawn
+# so that the projections have the same distributions as the configuration's
+# k, v, q and gate logit: x ~ N(0, 1); the k, v, q rows ~ N(0, s^2 / D) with s
+# the configuration's k/v/q scale; the gate row ~ N(0, 1 / D); one gate bias per
+# head, spread evenly over [gate_mu - 1, gate_mu + 1] so that the heads start
+# with different decay rates.
+
+def frontend_width(cfg: Config) -> int:
+    return cfg.H * cfg.V
+
+
+def frontend_rows(cfg: Config) -> int:
+    """Weight rows per head: K (k), V (v), K (q) and 1 (gate logit), in that order."""
+    return 2 * cfg.K + cfg.V + 1
+
+
+def generate_frontend(cfg: Config, seed: int = 0, D: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw x [B,T,D] and Wx [H, 2K+V+1, D] (bfloat16 bit patterns, uint16) and
+    the gate bias [H] (fp32), from their own generator stream (seed + 2_000_003)."""
+    B, H, K, V, T = cfg.B, cfg.H, cfg.K, cfg.V, cfg.T
+    D = frontend_width(cfg) if D is None else D
+    rng = np.random.default_rng(seed + 2_000_003)
+    s = 1.0 / math.sqrt(K) if cfg.qkv_scale == "rsqrtK" else 1.0
+    Wx = rng.standard_normal((H, frontend_rows(cfg), D)) * (1.0 / math.sqrt(D))
+    Wx[:, :2 * K + V] *= s
+    out = {"Wx": fp32_to_bf16_bits(Wx.astype(np.float32))}
+    del Wx
+    out["bias"] = (cfg.gate_mu + (np.linspace(-1.0, 1.0, H) if H > 1 else np.zeros(1))).astype(np.float32)
+    x = np.empty((B, T, D), dtype=np.uint16)
+    for b in range(B):  # row by row, so that full-size draws stay small in fp64
+        x[b] = fp32_to_bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
+    out["x"] = x
     return out
