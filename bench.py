@@ -68,6 +68,9 @@ def parse():
                     help="approximate CPU time for the oracle baseline sample (0 disables)")
     ap.add_argument("--train", action="store_true",
                     help="time the training step instead: m2rnn_fwd_save then m2rnn_bwd (bf16 workloads)")
+    ap.add_argument("--frontend", action="store_true",
+                    help="time the layer front-end (projections of x and the gate) and the front-end + "
+                         "recurrence forward instead")
     ap.add_argument("--segment", type=int, default=256,
                     help="--train: steps per segment of the recomputing training mode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -278,6 +281,125 @@ def train_bench(args, cfg, dev, x):
     print(json.dumps(res), flush=True)
 
 
+FRONT_METRIC = "M2RNN layer front-end (x -> k, v, q, f) tokens·heads/sec at K=V=128, 1×MI355X"
+
+
+def cpu_baseline_frontend(cfg, g, budget_s):
+    """The fp64 front-end oracle on the first tokens of every batch row."""
+    from oracle import m2rnn_frontend_ref
+
+    def run(ts):
+        t0 = time.perf_counter()
+        m2rnn_frontend_ref(g["x"][:, :ts], g["Wx"], g["bias"], K=cfg.K, V=cfg.V)
+        return time.perf_counter() - t0
+
+    probe = min(4, cfg.T)
+    dt = run(probe)
+    ts = int(min(cfg.T, max(probe, probe * budget_s / max(dt, 1e-6))))
+    dt = run(ts)
+    return {
+        "value": cfg.B * cfg.H * ts / dt,
+        "unit": "tok·heads/s",
+        "cores": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"fp64 numpy front-end oracle, all {cfg.B} batch rows x {cfg.H} heads of {cfg.name}, "
+                  f"first {ts} of {cfg.T} steps ({dt:.1f}s)",
+    }
+
+
+def frontend_bench(args, cfg):
+    """Times the front-end alone (the dominant kernel here) and the layer's
+    forward: front-end, then the recurrence on its outputs."""
+    import numpy as np
+    import torch
+
+    from non_linear_matrix_amd import m2rnn
+    from non_linear_matrix_amd.inputs import frontend_rows, frontend_width, generate, generate_frontend
+
+    B, H, T, K, V = cfg.B, cfg.H, cfg.T, cfg.K, cfg.V
+    D, R = frontend_width(cfg), frontend_rows(cfg)
+    g = generate_frontend(cfg, args.seed)
+    rec = generate(cfg.with_(T=1), args.seed)   # a W and an H0 of the right shapes (T = 1 keeps the draw small)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    x, Wx, bias, W = dev(g["x"]), dev(g["Wx"]), dev(g["bias"]), dev(rec["W"])
+    H0 = None if rec["H0"] is None else dev(rec["H0"])
+    stream = torch.cuda.current_stream()
+    out = m2rnn.frontend(x, Wx, bias, K=K, V=V, stream=stream)
+    y = torch.empty((B, H, T, V), dtype=torch.float32, device="cuda")
+    HT = torch.empty((B, H, K, V), dtype=torch.float32, device="cuda")
+
+    def front():
+        m2rnn.frontend(x, Wx, bias, K=K, V=V, out=out, stream=stream)
+
+    def layer():
+        front()
+        m2rnn.fwd(out["k"], out["v"], out["q"], out["f"], W, H0, y=y, H_T=HT, algo=args.algo, stream=stream)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    front_ms = timed(front, args.steps)
+    layer_ms = timed(layer, args.steps)
+    tokens = B * H * T
+    M, N = B * T, H * R
+    flops = 2.0 * M * N * D
+    # bytes the product must move once: x and Wx (bf16), bias, outputs (bf16)
+    algo_bytes = 2.0 * (M * D + N * D) + 4 * H + 2.0 * M * N
+    peak = PEAK_TFLOPS["bf16"]
+    achieved = flops / (front_ms * 1e-3) / 1e12
+    res = {
+        "metric": FRONT_METRIC,
+        "value": tokens / (front_ms * 1e-3),
+        "unit": "tok·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": front_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name} front-end: x [B={B}, T={T}, D={D}] bf16, Wx [H={H}, 2K+V+1={R}, D] bf16, "
+                        f"K={K} V={V}, seed {args.seed}",
+            "B": B, "H": H, "K": K, "V": V, "T": T, "D": D,
+            "parallelism": "one GPU; 128x128 output tiles across CUs",
+        },
+        "layer_fwd_ms": layer_ms,
+        "layer_fwd_tok_heads_per_s": tokens / (layer_ms * 1e-3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "kernel": "frontend_kernel",
+            "kernel_avg_ms": front_ms,
+            "flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": algo_bytes,
+        },
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline_frontend(cfg, g, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -299,6 +421,9 @@ def main():
         return
     m2rnn.load()
     cfg = {**CONFIGS, **SERVING}[args.workload]
+    if args.frontend:
+        frontend_bench(args, cfg)
+        return
     plan = m2rnn.get_plan(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V, cfg.dtype, args.algo)
     print(f"[bench] workload {cfg} plan {plan}", file=sys.stderr, flush=True)
     x = generate(cfg, args.seed)

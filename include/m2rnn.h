@@ -209,6 +209,31 @@ m2rnn_status m2rnn_bwd_recompute(const void* k, const void* v, const void* q, co
                                  int V, int segment, m2rnn_dtype in_dtype, m2rnn_algo algo,
                                  void* stream);
 
+/* ---- Layer front-end: the inputs of the recurrence from the layer input.
+ * The pages derive k_t, v_t (and q_t) from x_t and make the forget gate a
+ * parameterised function psi(x_t) of the input alone that keeps f_t in [0, 1],
+ * with different decay rates per head (zh summary §2.1). Read here as per-head
+ * linear projections and a logistic sigmoid with a per-head bias:
+ *   k_t = Wk_h x_t,  v_t = Wv_h x_t,  q_t = Wq_h x_t,
+ *   f_t = 1 / (1 + exp(-(w_h . x_t + bias_h))).
+ * One matrix product over the model width D with the sigmoid and the layout
+ * change fused into its epilogue.
+ *   x    [B][T][D] bf16, the layer input (row b T + t);
+ *   Wx   [H][2K + V + 1][D] bf16: per head K rows for k, V rows for v, K rows
+ *        for q, then the gate row;
+ *   bias [H] fp32 (4-byte aligned);
+ *   k, q [B][H][T][K], v [B][H][T][V], f [B][H][T]: bf16 outputs (round to
+ *        nearest even), exactly the inputs m2rnn_fwd and the training entry
+ *        points read.
+ * Accumulation is fp32. All pointers are device memory owned by the caller;
+ * x, Wx and the outputs 16-byte aligned. Asynchronous on `stream`.
+ * INVALID_VALUE: a NULL or misaligned pointer, a size < 1, sizes that overflow.
+ * NOT_SUPPORTED: in_dtype not BF16, K or V not in {16, 32, ..., 128}, D not a
+ * multiple of 8. */
+m2rnn_status m2rnn_frontend(const void* x, const void* Wx, const float* bias, void* k, void* v,
+                            void* q, void* f, int B, int T, int D, int H, int K, int V,
+                            m2rnn_dtype in_dtype, void* stream);
+
 /* Host-only argument check: returns exactly what m2rnn_fwd_algo would return
  * before launching, without touching the GPU. */
 m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const void* f, const void* W,
@@ -239,7 +264,7 @@ m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dt
 const char* m2rnn_status_string(m2rnn_status status);
 
 /* Library ABI version: major * 10000 + minor * 100 + patch (0.2.0 added
- * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones). */
+ * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones and the front-end). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

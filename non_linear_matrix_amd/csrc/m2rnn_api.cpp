@@ -199,6 +199,27 @@ m2rnn_status m2rnn_bwd_recompute(const void* k, const void* v, const void* q, co
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
 }
 
+m2rnn_status m2rnn_frontend(const void* x, const void* Wx, const float* bias, void* k, void* v,
+                            void* q, void* f, int B, int T, int D, int H, int K, int V,
+                            m2rnn_dtype in_dtype, void* stream) {
+  if (!x || !Wx || !bias || !k || !v || !q || !f) return M2RNN_ERROR_INVALID_VALUE;
+  if (B < 1 || T < 1 || D < 1 || H < 1 || K < 1 || V < 1) return M2RNN_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(Wx) || !aligned16(k) || !aligned16(v) || !aligned16(q) ||
+      !aligned16(f) || (reinterpret_cast<std::uintptr_t>(bias) & 3u))
+    return M2RNN_ERROR_INVALID_VALUE;
+  if (in_dtype != M2RNN_DTYPE_BF16) return M2RNN_ERROR_NOT_SUPPORTED;
+  if (!supported_dim(K) || !supported_dim(V) || D % 8 != 0) return M2RNN_ERROR_NOT_SUPPORTED;
+  // element counts: x (B T D), Wx (H R D), the outputs (B H T max(K, V))
+  const long double lim = 4.0e18L;
+  const long double R = 2.0L * K + V + 1;
+  if ((long double)B * T * D >= lim || (long double)H * R * D >= lim || (long double)H * R >= 2.0e9L ||
+      !counts_fit(B, H, T, K, V) || ((long double)B * T / 128 + 1) * ((long double)H * R / 128 + 1) >= 2.0e9L)
+    return M2RNN_ERROR_INVALID_VALUE;
+  m2rnn::FrontLaunch p{x, Wx, bias, k, v, q, f, B, T, D, H, K, V};
+  hipError_t e = m2rnn::launch_frontend(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+}
+
 m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                             m2rnn_algo algo, m2rnn_plan* plan) {
   if (!plan) return M2RNN_ERROR_INVALID_VALUE;

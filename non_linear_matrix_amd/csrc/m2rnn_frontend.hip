@@ -1,0 +1,194 @@
+// Layer front-end of M²RNN: the per-head projections of the layer input x_t
+// that the recurrence consumes, k_t, v_t, q_t, and the forget gate
+// f_t = psi(x_t) (gist.science technical summary (zh) §2.1: the gate depends on
+// x_t only and is kept in [0, 1] by a parameterised function, with per-head
+// decay rates). psi is read as the logistic sigmoid of a linear projection plus
+// a per-head bias.
+//
+// All of it is one matrix product over the model width D followed by a
+// per-column epilogue:
+//   P[m][n] = sum_d x[m][d] Wx[n][d],   m = b T + t,  n = h R + r,  R = 2K + V + 1
+// row r of head h feeds k (r < K), v (K <= r < K + V), q (K + V <= r < 2K + V) or
+// the gate logit (r = 2K + V), which gets the head's bias and the sigmoid. The
+// epilogue writes bf16 straight into the [B][H][T][*] layouts the recurrence
+// reads, so nothing else touches the projections.
+//
+// Kernel: 128 x 128 output tiles per workgroup of 4 waves (2 x 2 waves of
+// 64 x 64, each 4 x 4 tiles of v_mfma_f32_16x16x32_bf16). Both operands are
+// contiguous along D, so a lane's MFMA fragment (8 consecutive d of one row) is
+// one 16-byte LDS read. The k-loop stages 64-wide slices of x and Wx through
+// double-buffered LDS; the next slice's global reads are in flight while the
+// current one is multiplied. Tiles are dealt so that each XCD gets a contiguous
+// range, walked in groups of 8 tile rows, which keeps the x rows and the Wx
+// tiles in flight within one XCD's L2.
+#include <hip/hip_runtime.h>
+
+#include "m2rnn_internal.h"
+
+namespace m2rnn {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f4;
+typedef __attribute__((ext_vector_type(2))) float f2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u4;
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LROW = BK + 8;                   // bf16 per LDS row: 16 bytes of padding
+constexpr int THREADS = 256;
+constexpr int PPT = BM * BK / 8 / THREADS;     // 16-byte pieces per thread and operand
+constexpr int GROUP_M = 8;                     // tile rows walked together
+static_assert(BM == BN && PPT * THREADS * 8 == BM * BK, "tile shape");
+
+struct FrontArgs {
+  const unsigned short* x;   // [M][D]
+  const unsigned short* Wx;  // [N][D]
+  const float* bias;         // [H]
+  unsigned short *k, *v, *q, *f;
+  long long M;
+  int N, D, T, H, K, V, R;
+  int tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned short to_bf16(float x) {
+  const unsigned int p = __builtin_bit_cast(unsigned int, __builtin_convertvector(f2{x, 0.0f}, bf16x2));
+  return static_cast<unsigned short>(p & 0xffffu);
+}
+
+__global__ __launch_bounds__(THREADS, 2) void frontend_kernel(FrontArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned short As[2][BM * LROW];
+  __shared__ __attribute__((aligned(16))) unsigned short Bs[2][BN * LROW];
+  const int tid = threadIdx.x, w = tid / 64, l = tid % 64, g = l / 16, n = l % 16;
+  const int wm = w / 2, wn = w % 2;
+
+  // workgroup -> tile. Workgroups are dealt round-robin over the 8 XCDs; give
+  // XCD x the contiguous range of tiles [start(x), start(x) + count(x)).
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int per = nwg / 8, rem = nwg % 8, xcd = bid % 8;
+  const int tile = xcd * per + min(xcd, rem) + bid / 8;
+  // then groups of GROUP_M tile rows, column by column
+  const int in_group = GROUP_M * a.tiles_n;
+  const int first_m = (tile / in_group) * GROUP_M;
+  const int gsize = min(a.tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (tile % in_group) % gsize;
+  const int tn = (tile % in_group) / gsize;
+  const long long m0 = (long long)tm * BM;
+  const int n0 = tn * BN;
+
+  u4 ra[PPT], rb[PPT];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int p = tid + THREADS * r, row = p / (BK / 8), c8 = p % (BK / 8);
+      const int kc = k0 + 8 * c8;
+      const long long m = m0 + row;
+      const int nn = n0 + row;
+      ra[r] = u4{0, 0, 0, 0};
+      rb[r] = u4{0, 0, 0, 0};
+      if (m < a.M && kc < a.D) ra[r] = *reinterpret_cast<const u4*>(a.x + m * a.D + kc);
+      if (nn < a.N && kc < a.D) rb[r] = *reinterpret_cast<const u4*>(a.Wx + (long long)nn * a.D + kc);
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int p = tid + THREADS * r, row = p / (BK / 8), c8 = p % (BK / 8);
+      *reinterpret_cast<u4*>(&As[buf][row * LROW + 8 * c8]) = ra[r];
+      *reinterpret_cast<u4*>(&Bs[buf][row * LROW + 8 * c8]) = rb[r];
+    }
+  };
+
+  f4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0, 0, 0, 0};
+
+  const int nk = (a.D + BK - 1) / BK;
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) fetch((kt + 1) * BK);  // in flight during this slice's products
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8 A[4], Bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        A[i] = *reinterpret_cast<const bf16x8*>(&As[buf][(wm * 64 + 16 * i + n) * LROW + kk + 8 * g]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        Bf[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(wn * 64 + 16 * j + n) * LROW + kk + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(A[i], Bf[j], acc[i][j]);
+    }
+    // the other buffer was last read before the previous barrier
+    if (kt + 1 < nk) put(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane (g, n) of tile (i, j) holds P[m0 + 64 wm + 16 i + 4 g + e][n0 + 64 wn + 16 j + n]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int nn = n0 + wn * 64 + 16 * j + n;
+    if (nn >= a.N) continue;
+    const int h = nn / a.R, r = nn - h * a.R;
+    const float bh = a.bias[h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const long long m = m0 + wm * 64 + 16 * i + 4 * g + e;
+        if (m >= a.M) continue;
+        const long long b = m / a.T, t = m - b * a.T;
+        const long long row = (b * a.H + h) * a.T + t;  // (unit, step)
+        float val = acc[i][j][e];
+        if (r < a.K) {
+          a.k[row * a.K + r] = to_bf16(val);
+        } else if (r < a.K + a.V) {
+          a.v[row * a.V + (r - a.K)] = to_bf16(val);
+        } else if (r < 2 * a.K + a.V) {
+          a.q[row * a.K + (r - a.K - a.V)] = to_bf16(val);
+        } else {
+          a.f[row] = to_bf16(1.0f / (1.0f + __expf(-(val + bh))));
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_frontend(const FrontLaunch& p, hipStream_t stream) {
+  FrontArgs a{};
+  a.x = static_cast<const unsigned short*>(p.x);
+  a.Wx = static_cast<const unsigned short*>(p.Wx);
+  a.bias = p.bias;
+  a.k = static_cast<unsigned short*>(p.k);
+  a.v = static_cast<unsigned short*>(p.v);
+  a.q = static_cast<unsigned short*>(p.q);
+  a.f = static_cast<unsigned short*>(p.f);
+  a.M = (long long)p.B * p.T;
+  a.R = 2 * p.K + p.V + 1;
+  a.N = p.H * a.R;
+  a.D = p.D;
+  a.T = p.T;
+  a.H = p.H;
+  a.K = p.K;
+  a.V = p.V;
+  const long long tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+  if (tm * tn > 0x7fffffffLL || GROUP_M * tn > 0x7fffffffLL) return hipErrorInvalidValue;
+  a.tiles_m = static_cast<int>(tm);
+  a.tiles_n = static_cast<int>(tn);
+  hipLaunchKernelGGL(frontend_kernel, dim3(static_cast<unsigned>(tm * tn)), dim3(THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace m2rnn

@@ -80,6 +80,16 @@ hipError_t launch_fwd_ckpt(const FwdArgs& a, float* ckpt, int S, bool split, hip
 hipError_t launch_bwd_recompute(const BwdLaunch& p, const float* H0, const float* ckpt, int S, bool split,
                                 hipStream_t stream);
 
+// Layer front-end (m2rnn_frontend.hip): k, v, q and f from x (bf16).
+struct FrontLaunch {
+  const void* x;      // [B][T][D]
+  const void* Wx;     // [H][2K + V + 1][D]
+  const float* bias;  // [H]
+  void *k, *v, *q, *f;
+  int B, T, D, H, K, V;
+};
+hipError_t launch_frontend(const FrontLaunch& p, hipStream_t stream);
+
 struct Plan {
   int grid, block, rows_per_group, groups_per_unit, clears_y, lds_bytes;
 };

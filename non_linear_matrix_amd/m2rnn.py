@@ -85,6 +85,8 @@ def load() -> ctypes.CDLL:
     lib.m2rnn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, vp,
                               i, i, i, i, i, i, vp]
     lib.m2rnn_bwd.restype = i
+    lib.m2rnn_frontend.argtypes = [vp, vp, fp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.m2rnn_frontend.restype = i
     lib.m2rnn_ckpt_bytes.argtypes = [i, i, i, i, i, i]
     lib.m2rnn_ckpt_bytes.restype = u64
     lib.m2rnn_fwd_ckpt.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, i, i, i, vp]
@@ -354,4 +356,38 @@ def bwd_recompute(k, v, q, f, W, H0, ckpt, dy, dH_T=None, *, segment: int, algo:
     if st != 0:
         raise M2RNNError(st, "m2rnn_bwd_recompute")
     out["workspace"] = ws
+    return out
+
+
+def frontend(x, Wx, bias, *, K: int, V: int, out=None, stream=None) -> dict:
+    """Layer front-end (m2rnn_frontend): x [B,T,D] bf16, Wx [H, 2K+V+1, D] bf16,
+    bias [H] float32, all on the device. Returns dict(k, v, q, f) of bf16 device
+    tensors in the recurrence's layouts (pass `out`, a dict of the same, to reuse)."""
+    import torch
+
+    lib = load()
+    B, T, D = x.shape
+    H, R, D2 = Wx.shape
+    if D2 != D or R != 2 * K + V + 1 or tuple(bias.shape) != (H,):
+        raise ValueError("inconsistent shapes")
+    for t in (x, Wx, bias):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("x, Wx and bias must be contiguous device tensors")
+    if x.dtype != torch.bfloat16 or Wx.dtype != torch.bfloat16 or bias.dtype != torch.float32:
+        raise TypeError("x and Wx take bf16, bias float32")
+    dev = x.device
+    if out is None:
+        out = {
+            "k": torch.empty((B, H, T, K), dtype=torch.bfloat16, device=dev),
+            "v": torch.empty((B, H, T, V), dtype=torch.bfloat16, device=dev),
+            "q": torch.empty((B, H, T, K), dtype=torch.bfloat16, device=dev),
+            "f": torch.empty((B, H, T), dtype=torch.bfloat16, device=dev),
+        }
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib.m2rnn_frontend(x.data_ptr(), Wx.data_ptr(), bias.data_ptr(), out["k"].data_ptr(), out["v"].data_ptr(),
+                            out["q"].data_ptr(), out["f"].data_ptr(), B, T, D, H, K, V, DTYPES["bf16"],
+                            stream.cuda_stream)
+    if st != 0:
+        raise M2RNNError(st, "m2rnn_frontend")
     return out

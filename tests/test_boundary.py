@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported():
                           "m2rnn_check_args", "m2rnn_pick_algo", "m2rnn_status_string", "m2rnn_version",
                           "m2rnn_saved_bytes", "m2rnn_fwd_save", "m2rnn_bwd_workspace_bytes", "m2rnn_bwd",
                           "m2rnn_ckpt_bytes", "m2rnn_fwd_ckpt", "m2rnn_bwd_recompute_workspace_bytes",
-                          "m2rnn_bwd_recompute"}
+                          "m2rnn_bwd_recompute", "m2rnn_frontend"}
     raw = ctypes.CDLL(m2rnn.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), f"{name} declared in include/m2rnn.h but not exported"
@@ -185,3 +185,21 @@ def test_recompute_entry_points_validate_before_launching():
     assert bwd(p, 16, ws=None) == INVALID
     assert bwd(p, 16, dk=None) == INVALID
     assert bwd(p, 16, algo=simple) == UNSUPPORTED
+
+
+def test_frontend_validates_before_launching():
+    lib = m2rnn.load()
+    p = 0x10000
+    bf16 = m2rnn.DTYPES["bf16"]
+
+    def call(x=p, Wx=p, bias=p, k=p, B=2, T=3, D=64, H=2, K=64, V=64, dt=bf16):
+        return lib.m2rnn_frontend(x, Wx, bias, k, p, p, p, B, T, D, H, K, V, dt, None)
+    assert call(x=None) == INVALID
+    assert call(bias=None) == INVALID
+    assert call(x=p + 8) == INVALID          # misaligned
+    assert call(bias=p + 2) == INVALID
+    assert call(B=0) == INVALID
+    assert call(D=0) == INVALID
+    assert call(D=60) == UNSUPPORTED         # rows of x must be whole 16-byte pieces
+    assert call(K=40) == UNSUPPORTED
+    assert call(dt=m2rnn.DTYPES["f32"]) == UNSUPPORTED
