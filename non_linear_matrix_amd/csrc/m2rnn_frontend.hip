@@ -17,8 +17,8 @@
 // 64 x 64, each 4 x 4 tiles of v_mfma_f32_16x16x32_bf16). Both operands are
 // contiguous along D, so a lane's MFMA fragment (8 consecutive d of one row) is
 // one 16-byte LDS read. The k-loop stages 64-wide slices of x and Wx through
-// double-buffered LDS; the next slice's global reads are in flight while the
-// current one is multiplied. Tiles are dealt so that each XCD gets a contiguous
+// double-buffered LDS; the global reads of the next two slices are in flight
+// while the current one is multiplied. Tiles are dealt so that each XCD gets a contiguous
 // range, walked in groups of 8 tile rows, which keeps the x rows and the Wx
 // tiles in flight within one XCD's L2.
 #include <hip/hip_runtime.h>
@@ -80,26 +80,37 @@ __global__ __launch_bounds__(THREADS, 2) void frontend_kernel(FrontArgs a) {
   const long long m0 = (long long)tm * BM;
   const int n0 = tn * BN;
 
-  u4 ra[PPT], rb[PPT];
-  auto fetch = [&](int k0) {
+  // two register sets of global reads: slice j goes through set j % 2, so each
+  // slice's reads have two slices of products to land
+  u4 ra0[PPT], rb0[PPT], ra1[PPT], rb1[PPT];
+  // piece r of a slice is row tid / 8 + 32 r, columns 8 (tid % 8) .. + 7 of the slice
+  constexpr int RSTEP = THREADS / (BK / 8);
+  const int prow = tid / (BK / 8), pcol = 8 * (tid % (BK / 8));
+  const unsigned short* xp = a.x + (m0 + prow) * a.D + pcol;
+  const unsigned short* wp = a.Wx + (long long)(n0 + prow) * a.D + pcol;
+  unsigned int xok = 0, wok = 0;  // bit r: piece r's row exists
+#pragma unroll
+  for (int r = 0; r < PPT; ++r) {
+    xok |= (m0 + prow + RSTEP * r < a.M) ? 1u << r : 0u;
+    wok |= (n0 + prow + RSTEP * r < a.N) ? 1u << r : 0u;
+  }
+  const long long xstep = (long long)RSTEP * a.D;
+  auto fetch = [&](int k0, u4 (&xa)[PPT], u4 (&xb)[PPT]) {
+    const bool kin = k0 + pcol < a.D;
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
-      const int p = tid + THREADS * r, row = p / (BK / 8), c8 = p % (BK / 8);
-      const int kc = k0 + 8 * c8;
-      const long long m = m0 + row;
-      const int nn = n0 + row;
-      ra[r] = u4{0, 0, 0, 0};
-      rb[r] = u4{0, 0, 0, 0};
-      if (m < a.M && kc < a.D) ra[r] = *reinterpret_cast<const u4*>(a.x + m * a.D + kc);
-      if (nn < a.N && kc < a.D) rb[r] = *reinterpret_cast<const u4*>(a.Wx + (long long)nn * a.D + kc);
+      xa[r] = u4{0, 0, 0, 0};
+      xb[r] = u4{0, 0, 0, 0};
+      if (kin && ((xok >> r) & 1u)) xa[r] = *reinterpret_cast<const u4*>(xp + r * xstep + k0);
+      if (kin && ((wok >> r) & 1u)) xb[r] = *reinterpret_cast<const u4*>(wp + r * xstep + k0);
     }
   };
-  auto put = [&](int buf) {
+  auto put = [&](int buf, const u4 (&xa)[PPT], const u4 (&xb)[PPT]) {
 #pragma unroll
     for (int r = 0; r < PPT; ++r) {
-      const int p = tid + THREADS * r, row = p / (BK / 8), c8 = p % (BK / 8);
-      *reinterpret_cast<u4*>(&As[buf][row * LROW + 8 * c8]) = ra[r];
-      *reinterpret_cast<u4*>(&Bs[buf][row * LROW + 8 * c8]) = rb[r];
+      const int off = (prow + RSTEP * r) * LROW + pcol;
+      *reinterpret_cast<u4*>(&As[buf][off]) = xa[r];
+      *reinterpret_cast<u4*>(&Bs[buf][off]) = xb[r];
     }
   };
 
@@ -108,14 +119,7 @@ __global__ __launch_bounds__(THREADS, 2) void frontend_kernel(FrontArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f4{0, 0, 0, 0};
-
-  const int nk = (a.D + BK - 1) / BK;
-  fetch(0);
-  put(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) fetch((kt + 1) * BK);  // in flight during this slice's products
+  auto products = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       bf16x8 A[4], Bf[4];
@@ -130,38 +134,81 @@ __global__ __launch_bounds__(THREADS, 2) void frontend_kernel(FrontArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma(A[i], Bf[j], acc[i][j]);
     }
-    // the other buffer was last read before the previous barrier
-    if (kt + 1 < nk) put(buf ^ 1);
+  };
+
+  // slice j sits in LDS buffer j % 2; a buffer is rewritten only after the
+  // barrier that follows its last products
+  const int nk = (a.D + BK - 1) / BK;
+  fetch(0, ra0, rb0);
+  if (nk > 1) fetch(BK, ra1, rb1);
+  put(0, ra0, rb0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) fetch((kt + 2) * BK, ra0, rb0);
+    products(0);
+    if (kt + 1 < nk) put(1, ra1, rb1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    if (kt + 3 < nk) fetch((kt + 3) * BK, ra1, rb1);
+    products(1);
+    if (kt + 2 < nk) put(0, ra0, rb0);
     __syncthreads();
   }
 
-  // epilogue: lane (g, n) of tile (i, j) holds P[m0 + 64 wm + 16 i + 4 g + e][n0 + 64 wn + 16 j + n]
+  // epilogue: lane (g, n) of tile (i, j) holds P[m0 + 64 wm + 16 i + 4 g + e][n0 + 64 wn + 16 j + n].
+  // Per column: its head, output array and row length; per row: its (b, t),
+  // from one division per lane and then at most one wrap (T >= 64) per row.
+  unsigned short* dst[4];
+  int ldc[4], hj[4];
+  float bj[4];
+  bool gate[4], col_ok[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int nn = n0 + wn * 64 + 16 * j + n;
-    if (nn >= a.N) continue;
-    const int h = nn / a.R, r = nn - h * a.R;
-    const float bh = a.bias[h];
+    col_ok[j] = nn < a.N;
+    const int h = col_ok[j] ? nn / a.R : 0, r = nn - h * a.R;
+    hj[j] = h;
+    bj[j] = a.bias[h];
+    gate[j] = r == 2 * a.K + a.V;
+    if (r < a.K) {
+      dst[j] = a.k + r; ldc[j] = a.K;
+    } else if (r < a.K + a.V) {
+      dst[j] = a.v + (r - a.K); ldc[j] = a.V;
+    } else if (r < 2 * a.K + a.V) {
+      dst[j] = a.q + (r - a.K - a.V); ldc[j] = a.K;
+    } else {
+      dst[j] = a.f; ldc[j] = 1;
+    }
+  }
+  const long long mbase = m0 + wm * 64 + 4 * g;  // rows mbase + 16 i + e
+  const long long b0 = mbase / a.T;
+  const int t0 = static_cast<int>(mbase - b0 * a.T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const long long m = m0 + wm * 64 + 16 * i + 4 * g + e;
-        if (m >= a.M) continue;
-        const long long b = m / a.T, t = m - b * a.T;
-        const long long row = (b * a.H + h) * a.T + t;  // (unit, step)
-        float val = acc[i][j][e];
-        if (r < a.K) {
-          a.k[row * a.K + r] = to_bf16(val);
-        } else if (r < a.K + a.V) {
-          a.v[row * a.V + (r - a.K)] = to_bf16(val);
-        } else if (r < 2 * a.K + a.V) {
-          a.q[row * a.K + (r - a.K - a.V)] = to_bf16(val);
+    for (int e = 0; e < 4; ++e) {
+      const int o = 16 * i + e;
+      if (mbase + o >= a.M) continue;
+      long long b = b0;
+      int t = t0 + o;
+      if (t >= a.T) {
+        if (a.T >= 64) {
+          t -= a.T;
+          ++b;
         } else {
-          a.f[row] = to_bf16(1.0f / (1.0f + __expf(-(val + bh))));
+          b += t / a.T;
+          t %= a.T;
         }
       }
-  }
+      const long long bh = b * a.H;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!col_ok[j]) continue;
+        const long long row = (bh + hj[j]) * a.T + t;  // (unit, step)
+        const float val = acc[i][j][e];
+        dst[j][row * ldc[j]] = to_bf16(gate[j] ? 1.0f / (1.0f + __expf(-(val + bj[j]))) : val);
+      }
+    }
 }
 
 }  // namespace
