@@ -36,20 +36,26 @@ METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 # kernel source it was taken on; for any other source the traffic is unknown.
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
-    # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, sha256 of csrc/m2rnn_mfma.hip)
-    ("C3", "mfma"): (136486.4, 1056768.0, "e22dab9c5f5665e2f2dfa3dc5ea1b339e774643d46611105ebb487dc9a0d9a93"),
+    # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
+    ("C3", "mfma"): (136486.4, 1056768.0, "m2rnn_mfma.hip",
+                     "e22dab9c5f5665e2f2dfa3dc5ea1b339e774643d46611105ebb487dc9a0d9a93"),
+    ("D1", "mfma"): (267823.2, 530624.2, "m2rnn_decode.hip",
+                     "956ca12e91e2af7f990630af4aead6a5a4ebb04ffc1229b7d6494d0c06ac9e4f"),
 }
-KERNEL_SOURCE = os.path.join(ROOT, "non_linear_matrix_amd", "csrc", "m2rnn_mfma.hip")
+CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 
 
 def measured_traffic(workload, algo):
     import hashlib
 
     rec = TRAFFIC_KIB.get((workload, algo))
-    if rec is None or not os.path.exists(KERNEL_SOURCE):
+    if rec is None:
         return None
-    with open(KERNEL_SOURCE, "rb") as fh:
-        if hashlib.sha256(fh.read()).hexdigest() != rec[2]:
+    src = os.path.join(CSRC, rec[2])
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as fh:
+        if hashlib.sha256(fh.read()).hexdigest() != rec[3]:
             return None
     return 1024.0 * (rec[0] * COUNTER_SCALE["FETCH_SIZE"] + rec[1] * COUNTER_SCALE["WRITE_SIZE"])
 
@@ -522,7 +528,8 @@ def main():
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
             "frac": hbm_gbs / HBM_PEAK_GBS if hbm_bound else achieved / peak,
             "traffic": measured_traffic(args.workload, plan["algo"]),
-            "kernel": "mfma_fwd_kernel" if plan["algo"].startswith("mfma") else "simple_fwd_kernel",
+            "kernel": ("decode_kernel" if cfg.T == 1 else "mfma_fwd_kernel") if plan["algo"].startswith("mfma")
+                      else "simple_fwd_kernel",
             "kernel_avg_ms": kern_avg,
             "flops_per_launch": flops,
             "algorithmic_bytes_per_launch": algo_bytes,

@@ -228,9 +228,10 @@ m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dt
   m2rnn_status st = check(p, p, p, p, p, nullptr, pf, nullptr, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
   if (algo == M2RNN_ALGO_AUTO) algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
-  m2rnn::Plan pl = (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT)
-                       ? m2rnn::plan_mfma(B, H, K, V, algo == M2RNN_ALGO_MFMA_SPLIT)
-                       : m2rnn::plan_simple(B, H, K, V);
+  const bool mf = algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT;
+  m2rnn::Plan pl = !mf ? m2rnn::plan_simple(B, H, K, V)
+                   : T == 1 ? m2rnn::plan_decode(B, H, K, V)
+                            : m2rnn::plan_mfma(B, H, K, V, algo == M2RNN_ALGO_MFMA_SPLIT);
   if (pl.grid < 0) return M2RNN_ERROR_INVALID_VALUE;
   plan->algo = algo;
   plan->grid = pl.grid;

@@ -52,6 +52,11 @@ hipError_t launch_simple(const FwdArgs& a, hipStream_t stream);
 // split: state operand as bf16 hi + lo (two MFMA passes) instead of one bf16.
 hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream);
 bool mfma_supports(int K, int V, int bf16);
+// One-step kernel (m2rnn_decode.hip): T == 1, no saved data, bf16, MFMA shapes.
+// launch_mfma routes such calls to it; it writes y itself (no clearing needed).
+bool decode_supports(const FwdArgs& a);
+int decode_splits(int B, int H);
+hipError_t launch_decode(const FwdArgs& a, hipStream_t stream);
 // Fill n floats at p with zeros on `stream` (a kernel, so it can be captured).
 hipError_t fill_zero(float* p, long long n, hipStream_t stream);
 
@@ -95,5 +100,6 @@ struct Plan {
 };
 Plan plan_simple(int B, int H, int K, int V);
 Plan plan_mfma(int B, int H, int K, int V, bool split);
+Plan plan_decode(int B, int H, int K, int V);
 
 }  // namespace m2rnn
