@@ -51,6 +51,10 @@ SHAPES = [
     ("C3", dict(B=1, H=2, T=37)),                    # K = V = 128, two workgroups, ragged T
     ("C5", dict(B=2, H=1, T=16, K=32)),              # K = 32, V = 128, two-wave workgroups
     ("C3", dict(B=2, H=2, T=48, K=64, V=128)),
+    ("C3", dict(B=2, H=1, T=17, K=128, V=64)),       # K = 128, V = 64
+    ("C2", dict(B=1, H=3, T=33, K=32, V=64)),        # K = 32, V = 64
+    ("C3", dict(B=3, H=2, T=1)),                     # a single step
+    ("C5", dict(B=2, H=2, T=19)),                    # H0 = 0 (C5 starts from the zero state)
 ]
 
 
@@ -72,6 +76,24 @@ def test_without_final_state_gradient():
     got, ref = _grads(cfg, 32, with_dHT=False)
     for key in GRADS:
         assert nerr(got[key], ref[key]) <= TOL, key
+
+
+def test_without_initial_state_gradient():
+    import torch
+    from non_linear_matrix_amd import m2rnn
+
+    cfg = scaled(CONFIGS["C3"], B=1, H=2, T=21)
+    announce("bwd without dH0")
+    x = generate(cfg, 35)
+    d = to_device(x)
+    dy = torch.randn((cfg.B, cfg.H, cfg.T, cfg.V), generator=torch.Generator().manual_seed(7)).cuda()
+    _, _, saved = m2rnn.fwd_save(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"])
+    g0 = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, dy, want_dH0=False)
+    g1 = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, dy)
+    torch.cuda.synchronize()
+    assert g0["dH0"] is None
+    for key in ("dk", "dv", "dq", "df", "dW"):
+        assert torch.equal(g0[key], g1[key]), key
 
 
 def test_single_operand_forward_feeds_the_same_backward():
