@@ -37,8 +37,8 @@ METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
     # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
-    ("C3", "mfma"): (136486.4, 1056768.0, "m2rnn_mfma.hip",
-                     "e22dab9c5f5665e2f2dfa3dc5ea1b339e774643d46611105ebb487dc9a0d9a93"),
+    ("C3", "mfma"): (136485.5, 1056768.0, "m2rnn_mfma.hip",
+                     "1bc0c826cba1f59652c2940f5936aa56c2d4934b27d12aea700f6c8b1cf29904"),
     ("D1", "mfma"): (267823.2, 530624.2, "m2rnn_decode.hip",
                      "956ca12e91e2af7f990630af4aead6a5a4ebb04ffc1229b7d6494d0c06ac9e4f"),
 }
@@ -123,14 +123,38 @@ def cpu_baseline(cfg, x, budget_s):
     dt = run(probe)
     ts = int(min(cfg.T, max(probe, probe * budget_s / max(dt, 1e-6))))
     dt = run(ts)
-    return {
+    out = {
         "value": cfg.B * cfg.H * ts / dt,
         "unit": "tok·heads/s",
         "cores": threads if threads else os.cpu_count(),
         "kind": "oracle",
         "sample": f"fp64 numpy oracle, all {cfg.B * cfg.H} (b,h) units of {cfg.name}, first {ts} of {cfg.T} steps "
                   f"({dt:.1f}s); matmul on OpenBLAS threads, elementwise single-threaded",
+        "cpu_model": cpu_model(),
     }
+    # the same oracle held to one thread, on a quarter of the budget
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1 = run(probe)
+            t1 = int(min(cfg.T, max(probe, probe * budget_s / 4 / max(d1, 1e-6))))
+            d1 = run(t1)
+        out["single_thread_value"] = cfg.B * cfg.H * t1 / d1
+        out["single_thread_sample"] = f"first {t1} of {cfg.T} steps ({d1:.1f}s), one thread"
+    except Exception:
+        pass
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 TRAIN_METRIC = "M2RNN training step (fwd_save + bwd) tokens·heads/sec at K=V=128, 1×MI355X"
@@ -484,6 +508,7 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_avg = sum(kern_ms) / len(kern_ms)
+    kern_median = sorted(kern_ms)[len(kern_ms) // 2]
     ms_per_step = total_ms / args.steps
     tokens = cfg.H * (int(lens.sum()) if lens is not None else cfg.B * cfg.T)
     value = tokens / (ms_per_step * 1e-3)
@@ -531,9 +556,11 @@ def main():
             "kernel": ("decode_kernel" if cfg.T == 1 else "mfma_fwd_kernel") if plan["algo"].startswith("mfma")
                       else "simple_fwd_kernel",
             "kernel_avg_ms": kern_avg,
+            "kernel_median_ms": kern_median,
             "flops_per_launch": flops,
             "algorithmic_bytes_per_launch": algo_bytes,
         },
+        "hbm_GBps_algorithmic": hbm_gbs,
         "wall_s": wall,
     }
     if args.cpu_seconds > 0:
