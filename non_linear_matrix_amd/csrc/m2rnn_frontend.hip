@@ -16,9 +16,10 @@
 // Kernel: 128 x 128 output tiles per workgroup of 4 waves (2 x 2 waves of
 // 64 x 64, each 4 x 4 tiles of v_mfma_f32_16x16x32_bf16). Both operands are
 // contiguous along D, so a lane's MFMA fragment (8 consecutive d of one row) is
-// one 16-byte LDS read. The k-loop stages 64-wide slices of x and Wx through
-// double-buffered LDS; the global reads of the next two slices are in flight
-// while the current one is multiplied. Tiles are dealt so that each XCD gets a contiguous
+// one 16-byte LDS read. The k-loop stages 32-wide slices of x and Wx through
+// double-buffered LDS (40 KB, 124 VGPRs: four workgroups per CU, whose waves
+// hide each other's barrier and load latencies); the global reads of the next
+// slice are in flight while the current one is multiplied. Tiles are dealt so that each XCD gets a contiguous
 // range, walked in groups of 8 tile rows, which keeps the x rows and the Wx
 // tiles in flight within one XCD's L2.
 #include <hip/hip_runtime.h>
@@ -34,7 +35,7 @@ typedef __attribute__((ext_vector_type(2))) float f2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) unsigned int u4;
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int LROW = BK + 8;                   // bf16 per LDS row: 16 bytes of padding
 constexpr int THREADS = 256;
 constexpr int PPT = BM * BK / 8 / THREADS;     // 16-byte pieces per thread and operand
@@ -60,7 +61,7 @@ __device__ __forceinline__ unsigned short to_bf16(float x) {
   return static_cast<unsigned short>(p & 0xffffu);
 }
 
-__global__ __launch_bounds__(THREADS, 2) void frontend_kernel(FrontArgs a) {
+__global__ __launch_bounds__(THREADS, 4) void frontend_kernel(FrontArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned short As[2][BM * LROW];
   __shared__ __attribute__((aligned(16))) unsigned short Bs[2][BN * LROW];
   const int tid = threadIdx.x, w = tid / 64, l = tid % 64, g = l / 16, n = l % 16;
@@ -80,9 +81,8 @@ __global__ __launch_bounds__(THREADS, 2) void frontend_kernel(FrontArgs a) {
   const long long m0 = (long long)tm * BM;
   const int n0 = tn * BN;
 
-  // two register sets of global reads: slice j goes through set j % 2, so each
-  // slice's reads have two slices of products to land
-  u4 ra0[PPT], rb0[PPT], ra1[PPT], rb1[PPT];
+  // global reads of the next slice, staged in registers
+  u4 ra0[PPT], rb0[PPT];
   // piece r of a slice is row tid / 8 + 32 r, columns 8 (tid % 8) .. + 7 of the slice
   constexpr int RSTEP = THREADS / (BK / 8);
   const int prow = tid / (BK / 8), pcol = 8 * (tid % (BK / 8));
@@ -140,18 +140,13 @@ __global__ __launch_bounds__(THREADS, 2) void frontend_kernel(FrontArgs a) {
   // barrier that follows its last products
   const int nk = (a.D + BK - 1) / BK;
   fetch(0, ra0, rb0);
-  if (nk > 1) fetch(BK, ra1, rb1);
   put(0, ra0, rb0);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) fetch((kt + 2) * BK, ra0, rb0);
-    products(0);
-    if (kt + 1 < nk) put(1, ra1, rb1);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) fetch((kt + 3) * BK, ra1, rb1);
-    products(1);
-    if (kt + 2 < nk) put(0, ra0, rb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) fetch((kt + 1) * BK, ra0, rb0);
+    products(buf);
+    if (kt + 1 < nk) put(buf ^ 1, ra0, rb0);
     __syncthreads();
   }
 
