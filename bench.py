@@ -43,12 +43,16 @@ TRAFFIC_KIB = {
                      "956ca12e91e2af7f990630af4aead6a5a4ebb04ffc1229b7d6494d0c06ac9e4f"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
+# the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the
+# same counters summed over its kernels, and the source they were taken on
+TRAIN_TRAFFIC_KIB = (8659882.0 + 8388694.7 + 32786.1, 9743104.8 + 65560.2 + 1024.0, "m2rnn_bwd.hip",
+                     "f47d14a541bda0370c21fbbc9b3fe4a133cffebd3bb89be966c09dad4ced1a88")
 
 
 def measured_traffic(workload, algo):
     import hashlib
 
-    rec = TRAFFIC_KIB.get((workload, algo))
+    rec = TRAIN_TRAFFIC_KIB if (workload, algo) == ("C3", "train") else TRAFFIC_KIB.get((workload, algo))
     if rec is None:
         return None
     src = os.path.join(CSRC, rec[2])
@@ -299,7 +303,9 @@ def train_bench(args, cfg, dev, x):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name, "train") if best == "save" else None,
+            "traffic_GBps": (measured_traffic(cfg.name, "train") / (bwd_ms * 1e-3) / 1e9
+                             if best == "save" and measured_traffic(cfg.name, "train") else None),
             "kernel": f"backward call of mode {best}",
             "kernel_avg_ms": bwd_ms,
             "flops_per_launch": bwd_flops,
@@ -523,6 +529,28 @@ def main():
     hbm_bound = algo_bytes / (HBM_PEAK_GBS * 1e9) > flops / (peak * 1e12)
     achieved = flops / (kern_avg * 1e-3) / 1e12
     hbm_gbs = algo_bytes / (kern_avg * 1e-3) / 1e9
+    # the other matrix-core variant on the same workload, for reference (not `value`)
+    alt = None
+    if args.algo in ("mfma", "mfma_split") and cfg.T > 1:
+        other = "mfma_split" if args.algo == "mfma" else "mfma"
+        def alt_step():
+            if clear_here:
+                y.zero_()
+            m2rnn.fwd(dev["k"], dev["v"], dev["q"], dev["f"], dev["W"], dev["H0"], y=y, H_T=HT,
+                      seq_len=seq_len, algo=other, stream=stream, accumulate_y=clear_here)
+        for _ in range(3):
+            alt_step()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_alt = max(5, args.steps // 2)
+        a0.record(stream)
+        for _ in range(n_alt):
+            alt_step()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        alt_ms = a0.elapsed_time(a1) / n_alt
+        alt = {"algo": other, "ms_per_step": alt_ms, "tok_heads_per_s": tokens / (alt_ms * 1e-3),
+               "note": "mfma_split is what algo AUTO picks (the precise operand); not the headline value"}
     out = {
         "metric": METRIC,
         "value": value,
@@ -561,6 +589,7 @@ def main():
             "algorithmic_bytes_per_launch": algo_bytes,
         },
         "hbm_GBps_algorithmic": hbm_gbs,
+        "other_variant": alt,
         "wall_s": wall,
     }
     if args.cpu_seconds > 0:
