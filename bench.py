@@ -8,10 +8,11 @@ K=V=128 configuration the headline metric is quoted on).
 Prints ONE JSON line (rank 0). Usage:
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload C3] [--algo mfma]
 
-The default kernel family is "mfma": the state enters the matrix product as one
-bf16 operand per step, the precision the design specifies, which meets the 2e-2
-bound on this workload (the GPU parity tests check it); "mfma_split" and
-"simple" can be timed with --algo. The GPU's clock ramps over the first few
+The default kernel family on this workload is "mfma": the state enters the
+matrix product as one bf16 operand per step, the precision the design
+specifies, which meets the 2e-2 bound here (the GPU parity tests check it);
+other workloads default to the library's automatic choice, and any family can
+be timed with --algo. The GPU's clock ramps over the first few
 launches, hence the warmup.
 """
 from __future__ import annotations
@@ -72,7 +73,9 @@ def parse():
     ap.add_argument("--workload", default="C3",
                     help="C1..C5 (the parity configurations), D1 (one decoding step, state in place) "
                          "or R1 (C3's shape with ragged lengths)")
-    ap.add_argument("--algo", default="mfma")
+    ap.add_argument("--algo", default=None,
+                    help="kernel family; default: mfma on C3, D1 and R1 (one bf16 operand per step meets the "
+                         "bar there), AUTO's choice on the other workloads")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time for the oracle baseline sample (0 disables)")
@@ -213,7 +216,7 @@ def train_bench(args, cfg, dev, x):
     dy = torch.randn((B, H, T, V), dtype=torch.float32, device="cuda", generator=g)
     y = torch.empty((B, H, T, V), dtype=torch.float32, device="cuda")
     HT = torch.empty((B, H, K, V), dtype=torch.float32, device="cuda")
-    algo = args.algo if args.algo != "mfma" else "mfma_split"
+    algo = args.algo if args.algo not in (None, "mfma") else "mfma_split"
     k, v, q, f, W, H0 = (dev[n] for n in ("k", "v", "q", "f", "W", "H0"))
 
     def timed(fwd, bwd):
@@ -374,7 +377,7 @@ def frontend_bench(args, cfg):
 
     def layer():
         front()
-        m2rnn.fwd(out["k"], out["v"], out["q"], out["f"], W, H0, y=y, H_T=HT, algo=args.algo, stream=stream)
+        m2rnn.fwd(out["k"], out["v"], out["q"], out["f"], W, H0, y=y, H_T=HT, algo=args.algo or "mfma", stream=stream)
 
     def timed(fn, steps):
         for _ in range(args.warmup):
@@ -460,7 +463,10 @@ def main():
     if args.frontend:
         frontend_bench(args, cfg)
         return
-    plan = m2rnn.get_plan(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V, cfg.dtype, args.algo)
+    if args.algo is None and not args.train:
+        args.algo = "mfma" if cfg.name in ("C3", "D1", "R1") else m2rnn.pick_algo(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V,
+                                                                                   cfg.dtype)
+    plan = m2rnn.get_plan(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V, cfg.dtype, args.algo or "auto")
     print(f"[bench] workload {cfg} plan {plan}", file=sys.stderr, flush=True)
     x = generate(cfg, args.seed)
     dev = {}
@@ -531,8 +537,9 @@ def main():
     hbm_gbs = algo_bytes / (kern_avg * 1e-3) / 1e9
     # the other matrix-core variant on the same workload, for reference (not `value`)
     alt = None
-    if args.algo in ("mfma", "mfma_split") and cfg.T > 1:
-        other = "mfma_split" if args.algo == "mfma" else "mfma"
+    if args.algo in ("mfma", "mfma_split", "mfma_long", "mfma_long_split") and cfg.T > 1:
+        other = {"mfma": "mfma_split", "mfma_split": "mfma", "mfma_long": "mfma_long_split",
+                 "mfma_long_split": "mfma_long"}[args.algo]
         def alt_step():
             if clear_here:
                 y.zero_()
@@ -550,7 +557,7 @@ def main():
         torch.cuda.synchronize()
         alt_ms = a0.elapsed_time(a1) / n_alt
         alt = {"algo": other, "ms_per_step": alt_ms, "tok_heads_per_s": tokens / (alt_ms * 1e-3),
-               "note": "mfma_split is what algo AUTO picks (the precise operand); not the headline value"}
+               "note": "the other operand variant of the same kernel family; not the headline value"}
     out = {
         "metric": METRIC,
         "value": value,
@@ -581,8 +588,9 @@ def main():
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
             "frac": hbm_gbs / HBM_PEAK_GBS if hbm_bound else achieved / peak,
             "traffic": measured_traffic(args.workload, plan["algo"]),
-            "kernel": ("decode_kernel" if cfg.T == 1 else "mfma_fwd_kernel") if plan["algo"].startswith("mfma")
-                      else "simple_fwd_kernel",
+            "kernel": ("decode_kernel" if cfg.T == 1 else
+                       "mfma_fwd_long_kernel" if plan["algo"].startswith("mfma_long") else "mfma_fwd_kernel")
+                      if plan["algo"].startswith("mfma") else "simple_fwd_kernel",
             "kernel_avg_ms": kern_avg,
             "kernel_median_ms": kern_median,
             "flops_per_launch": flops,

@@ -76,12 +76,26 @@ typedef enum m2rnn_dtype {
  *             2^-9 relative, which a sensitive trajectory can amplify.
  * MFMA_SPLIT: as MFMA with the state operand split into bf16 hi + bf16 lo and
  *             two MFMA passes (~2^-17 relative operand error).
- * AUTO:       MFMA_SPLIT where it covers the shape, else SIMPLE. */
+ * AUTO:       bf16 with V in {64, 128}, T > 1 and at most 512 16-row tiles
+ *             (B H K / 16 <= 512: two workgroups per CU of a 256-CU gfx950):
+ *             MFMA_LONG_SPLIT; else MFMA_SPLIT where it covers the shape, else
+ *             SIMPLE. With M2RNN_FLAG_DETERMINISTIC it never takes MFMA_LONG*.
+ * MFMA_LONG, MFMA_LONG_SPLIT: the same arithmetic as MFMA / MFMA_SPLIT, for
+ *             workloads with few 16-row tiles (B H K / 16 well below the GPU's
+ *             1024 SIMDs: small batches, long sequences). Each tile's V columns
+ *             are spread over V/32 waves that exchange the state operand through
+ *             LDS every step, which cuts the per-step latency; each tile is its
+ *             own workgroup, so y is summed over a unit's K/16 tiles with atomic
+ *             adds whose order, and hence y's last bits, can vary between runs
+ *             (H_T cannot). bf16, K in {16, ..., 128}, V in {64, 128}; forward
+ *             entry points only (the training ones return NOT_SUPPORTED). */
 typedef enum m2rnn_algo {
   M2RNN_ALGO_AUTO = 0,
   M2RNN_ALGO_SIMPLE = 1,
   M2RNN_ALGO_MFMA = 2,
-  M2RNN_ALGO_MFMA_SPLIT = 3
+  M2RNN_ALGO_MFMA_SPLIT = 3,
+  M2RNN_ALGO_MFMA_LONG = 4,
+  M2RNN_ALGO_MFMA_LONG_SPLIT = 5
 } m2rnn_algo;
 
 /* The forward recurrence with the automatically chosen kernel. */
@@ -100,7 +114,11 @@ enum {
   /* Add the readout into y instead of overwriting it: y[b][h][t][:] += H_t^T q_t.
    * The library then never clears y itself, so a caller that zeroes y first
    * gets the plain result with the recurrence as the only kernel on the stream. */
-  M2RNN_FLAG_ACCUMULATE_Y = 1u
+  M2RNN_FLAG_ACCUMULATE_Y = 1u,
+  /* Every output bitwise repeatable from run to run: AUTO then keeps to the
+   * kernels whose y has a fixed summation order, and MFMA_LONG* with T > 1
+   * (whose y adds over row tiles are atomic) is NOT_SUPPORTED. */
+  M2RNN_FLAG_DETERMINISTIC = 2u
 };
 
 /* m2rnn_fwd_algo with flags (a bitwise OR of M2RNN_FLAG_*; unknown bits are
@@ -241,7 +259,8 @@ m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const
                               int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                               m2rnn_algo algo);
 
-/* The kernel family AUTO resolves to for a shape (never AUTO; host only). */
+/* The kernel family AUTO resolves to for a shape without flags (never AUTO;
+ * host only). */
 m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype);
 
 /* Launch plan of one call (host only, no GPU access). */
@@ -264,7 +283,8 @@ m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dt
 const char* m2rnn_status_string(m2rnn_status status);
 
 /* Library ABI version: major * 10000 + minor * 100 + patch (0.2.0 added
- * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones and the front-end). */
+ * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones and the front-end, 0.4.0 MFMA_LONG, 0.5.0 AUTO's
+ * choice of MFMA_LONG_SPLIT and M2RNN_FLAG_DETERMINISTIC). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

@@ -41,6 +41,9 @@ m2rnn_status check(const void* k, const void* v, const void* q, const void* f, c
     case M2RNN_ALGO_MFMA_SPLIT:
       return m2rnn::mfma_supports(K, V, dt == M2RNN_DTYPE_BF16) ? M2RNN_SUCCESS
                                                                  : M2RNN_ERROR_NOT_SUPPORTED;
+    case M2RNN_ALGO_MFMA_LONG:
+    case M2RNN_ALGO_MFMA_LONG_SPLIT:
+      return (dt == M2RNN_DTYPE_BF16 && (V == 64 || V == 128)) ? M2RNN_SUCCESS : M2RNN_ERROR_NOT_SUPPORTED;
     default:
       return M2RNN_ERROR_NOT_SUPPORTED;
   }
@@ -58,9 +61,13 @@ m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const
 }
 
 m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype) {
-  (void)B;
-  (void)H;
-  (void)T;
+  // The latency-oriented kernel gives each 16-row tile a workgroup of V/32 waves;
+  // up to two such workgroups per CU of a 256-CU gfx950 it beats one wave per
+  // tile, beyond that the multi-step kernel's one wave per tile wins.
+  constexpr long double kLongMaxTiles = 512;
+  if (in_dtype == M2RNN_DTYPE_BF16 && T > 1 && (V == 64 || V == 128) && supported_dim(K) &&
+      (long double)B * H * (K / 16) <= kLongMaxTiles)
+    return M2RNN_ALGO_MFMA_LONG_SPLIT;
   if (m2rnn::mfma_supports(K, V, in_dtype == M2RNN_DTYPE_BF16)) return M2RNN_ALGO_MFMA_SPLIT;
   return M2RNN_ALGO_SIMPLE;
 }
@@ -72,14 +79,27 @@ m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const
   m2rnn_status st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
   if (seq_len && (reinterpret_cast<std::uintptr_t>(seq_len) & 3u) != 0) return M2RNN_ERROR_INVALID_VALUE;
-  if ((flags & ~static_cast<unsigned>(M2RNN_FLAG_ACCUMULATE_Y)) != 0u) return M2RNN_ERROR_NOT_SUPPORTED;
-  if (algo == M2RNN_ALGO_AUTO) algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
+  if ((flags & ~static_cast<unsigned>(M2RNN_FLAG_ACCUMULATE_Y | M2RNN_FLAG_DETERMINISTIC)) != 0u)
+    return M2RNN_ERROR_NOT_SUPPORTED;
+  const bool det = (flags & M2RNN_FLAG_DETERMINISTIC) != 0u;
+  if (algo == M2RNN_ALGO_AUTO) {
+    algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
+    if (det && (algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT))
+      algo = algo == M2RNN_ALGO_MFMA_LONG ? M2RNN_ALGO_MFMA : M2RNN_ALGO_MFMA_SPLIT;
+  }
+  // the long kernels sum y over row tiles with atomic adds (T = 1 takes the
+  // decoding kernel, which does not)
+  if (det && T > 1 && (algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT))
+    return M2RNN_ERROR_NOT_SUPPORTED;
   m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype == M2RNN_DTYPE_BF16 ? 1 : 0,
                    (flags & M2RNN_FLAG_ACCUMULATE_Y) ? 1 : 0, seq_len, nullptr};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT)
     e = m2rnn::launch_mfma(a, algo == M2RNN_ALGO_MFMA_SPLIT, s);
+  else if (algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT)
+    e = m2rnn::decode_supports(a) ? m2rnn::launch_decode(a, s)  // one step: the decoding kernel
+                                  : m2rnn::launch_long(a, algo == M2RNN_ALGO_MFMA_LONG_SPLIT, s);
   else
     e = m2rnn::launch_simple(a, s);
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
@@ -229,9 +249,11 @@ m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dt
   if (st != M2RNN_SUCCESS) return st;
   if (algo == M2RNN_ALGO_AUTO) algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
   const bool mf = algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT;
-  m2rnn::Plan pl = !mf ? m2rnn::plan_simple(B, H, K, V)
-                   : T == 1 ? m2rnn::plan_decode(B, H, K, V)
-                            : m2rnn::plan_mfma(B, H, K, V, algo == M2RNN_ALGO_MFMA_SPLIT);
+  const bool lg = algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT;
+  m2rnn::Plan pl = !(mf || lg) ? m2rnn::plan_simple(B, H, K, V)
+                   : T == 1 && m2rnn::mfma_supports(K, V, 1) ? m2rnn::plan_decode(B, H, K, V)
+                   : lg ? m2rnn::plan_long(B, H, K, V)
+                        : m2rnn::plan_mfma(B, H, K, V, algo == M2RNN_ALGO_MFMA_SPLIT);
   if (pl.grid < 0) return M2RNN_ERROR_INVALID_VALUE;
   plan->algo = algo;
   plan->grid = pl.grid;
@@ -259,6 +281,6 @@ const char* m2rnn_status_string(m2rnn_status status) {
   }
 }
 
-int m2rnn_version(void) { return 300; }
+int m2rnn_version(void) { return 500; }
 
 }  // extern "C"

@@ -101,5 +101,10 @@ struct Plan {
 Plan plan_simple(int B, int H, int K, int V);
 Plan plan_mfma(int B, int H, int K, int V, bool split);
 Plan plan_decode(int B, int H, int K, int V);
+// Latency-oriented forward (m2rnn_long.hip): one workgroup of V/32 waves per
+// 16-row tile; y summed over the tiles with atomic adds.
+bool long_supports(const FwdArgs& a);
+Plan plan_long(int B, int H, int K, int V);
+hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream);
 
 }  // namespace m2rnn

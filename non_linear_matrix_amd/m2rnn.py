@@ -14,15 +14,17 @@ __all__ = [
     "LIB_PATH", "M2RNNError", "load", "fwd", "check_args", "pick_algo", "status_string", "version",
     "fwd_save", "bwd", "saved_bytes", "bwd_workspace_bytes",
     "STATUS", "ALGOS", "DTYPES", "declared_functions", "get_plan", "Plan", "FLAG_ACCUMULATE_Y",
+    "FLAG_DETERMINISTIC",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm2rnn.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "m2rnn.h")
 
 STATUS = {0: "M2RNN_SUCCESS", 1: "M2RNN_ERROR_INVALID_VALUE", 2: "M2RNN_ERROR_NOT_SUPPORTED", 3: "M2RNN_ERROR_LAUNCH"}
-ALGOS = {"auto": 0, "simple": 1, "mfma": 2, "mfma_split": 3}
+ALGOS = {"auto": 0, "simple": 1, "mfma": 2, "mfma_split": 3, "mfma_long": 4, "mfma_long_split": 5}
 DTYPES = {"f32": 0, "bf16": 1}
 FLAG_ACCUMULATE_Y = 1
+FLAG_DETERMINISTIC = 2
 
 _lib = None
 
@@ -132,7 +134,8 @@ def declared_functions() -> list:
 
 
 def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, seq_len=None, algo: str = "auto", stream=None,
-        want_state: bool = True, accumulate_y: bool = False) -> Tuple["object", Optional["object"]]:
+        want_state: bool = True, accumulate_y: bool = False,
+        deterministic: bool = False) -> Tuple["object", Optional["object"]]:
     """Run the forward recurrence on torch device tensors.
 
     k, q [B,H,T,K]; v [B,H,T,V]; f [B,H,T]; W [H,V,V] — all torch.bfloat16 or all
@@ -141,7 +144,8 @@ def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, seq_len=None, algo: str = "
     seq_len: optional int32 device tensor [B] of per-sequence lengths
     (m2rnn_fwd_varlen); H_T may then be H0 itself for in-place continuation.
     Returns (y, H_T) (H_T is None when want_state is False and none was given).
-    accumulate_y adds the readout into the given y (M2RNN_FLAG_ACCUMULATE_Y).
+    accumulate_y adds the readout into the given y (M2RNN_FLAG_ACCUMULATE_Y);
+    deterministic asks for bitwise repeatable outputs (M2RNN_FLAG_DETERMINISTIC).
     """
     import torch
 
@@ -184,7 +188,8 @@ def fwd(k, v, q, f, W, H0=None, *, y=None, H_T=None, seq_len=None, algo: str = "
     ptr = lambda t: None if t is None else t.data_ptr()
     st = lib.m2rnn_fwd_varlen(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(y), ptr(H_T),
                               ptr(seq_len), B, H, T, K, V, dt, ALGOS[algo],
-                              FLAG_ACCUMULATE_Y if accumulate_y else 0, stream.cuda_stream)
+                              (FLAG_ACCUMULATE_Y if accumulate_y else 0)
+                              | (FLAG_DETERMINISTIC if deterministic else 0), stream.cuda_stream)
     if st != 0:
         raise M2RNNError(st, "m2rnn_fwd")
     return y, H_T

@@ -28,7 +28,7 @@ def _check(**over):
 def test_library_exists_and_loads():
     assert os.path.exists(m2rnn.LIB_PATH), "build the library first (python -m non_linear_matrix_amd.build)"
     lib = m2rnn.load()
-    assert m2rnn.version() == 300
+    assert m2rnn.version() == 500
 
 
 def test_every_declared_symbol_is_exported():
@@ -116,16 +116,41 @@ def test_launch_plans():
 
 def test_unknown_flag_bits_are_rejected():
     lib = m2rnn.load()
-    st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 1, 4, 64, 64, 1, 0, 2, None)
-    assert st == UNSUPPORTED
+    for bad in (4, 0x80000000, 4 | m2rnn.FLAG_ACCUMULATE_Y):
+        st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 1, 4, 64, 64, 1, 0, bad, None)
+        assert st == UNSUPPORTED, bad
     st = lib.m2rnn_fwd_ex(None, A, A, A, A, None, A, None, 1, 1, 4, 64, 64, 1, 0, 1, None)
     assert st == INVALID
 
 
 def test_auto_picks_a_kernel_that_covers_the_shape():
-    assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "bf16") == "mfma_split"
+    assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "bf16") == "mfma_split"     # 1024 row tiles
     assert m2rnn.pick_algo(1, 1, 64, 16, 16, "f32") == "simple"
-    assert m2rnn.pick_algo(1, 1, 64, 16, 128, "bf16") == "simple"
+    assert m2rnn.pick_algo(1, 1, 64, 16, 96, "bf16") == "simple"
+    # up to 512 16-row tiles (two workgroups per CU): the latency-oriented kernel
+    assert m2rnn.pick_algo(1, 1, 64, 16, 128, "bf16") == "mfma_long_split"
+    assert m2rnn.pick_algo(1, 32, 8192, 128, 128, "bf16") == "mfma_long_split"
+    assert m2rnn.pick_algo(2, 16, 32768, 64, 128, "bf16") == "mfma_long_split"
+    assert m2rnn.pick_algo(4, 8, 512, 64, 64, "bf16") == "mfma_long_split"
+    assert m2rnn.pick_algo(4, 16, 100, 128, 128, "bf16") == "mfma_long_split"  # 512 tiles
+    assert m2rnn.pick_algo(5, 16, 100, 128, 128, "bf16") == "mfma_split"       # 640 tiles
+    assert m2rnn.pick_algo(1, 32, 1, 128, 128, "bf16") == "mfma_split"         # one step: decoding kernel
+    assert m2rnn.pick_algo(1, 4, 64, 32, 64, "f32") == "simple"
+    p = m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "auto")
+    assert p["algo"] == "mfma_long_split" and p["grid"] == 256 and p["block"] == 256 and p["clears_y"] == 1
+
+
+def test_deterministic_flag_refuses_the_atomic_kernels():
+    """M2RNN_FLAG_DETERMINISTIC: explicit MFMA_LONG* with T > 1 is refused before
+    any launch (their y adds over row tiles are atomic)."""
+    lib = m2rnn.load()
+    det = m2rnn.FLAG_DETERMINISTIC
+    for algo in ("mfma_long", "mfma_long_split"):
+        st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 2, 16, 64, 128, 1, m2rnn.ALGOS[algo], det, None)
+        assert st == UNSUPPORTED, algo
+        st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 2, 16, 64, 128, 1, m2rnn.ALGOS[algo],
+                              det | m2rnn.FLAG_ACCUMULATE_Y, None)
+        assert st == UNSUPPORTED, algo
 
 
 def test_binding_refuses_host_tensors():

@@ -108,7 +108,7 @@ def test_qkv_scale_alternative_reading(algo):
     assert nerr(y, yr) <= _tol(cfg, algo) and nerr(HT, HTr) <= _tol(cfg, algo)
 
 
-@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split"])
+@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split", "mfma_long", "mfma_long_split"])
 def test_h0_null_equals_zero_state_and_state_optional(algo):
     import torch
     from non_linear_matrix_amd import m2rnn
@@ -122,10 +122,15 @@ def test_h0_null_equals_zero_state_and_state_optional(algo):
     y3, HT3 = m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], None, algo=algo, want_state=False)
     torch.cuda.synchronize()
     assert HT3 is None
-    assert torch.equal(y1, y2) and torch.equal(HT1, HT2) and torch.equal(y1, y3)
+    assert torch.equal(HT1, HT2)
+    if algo.startswith("mfma_long"):  # y summed over row tiles with atomic adds: rounding-level differences
+        yn = y1.abs().max().item()
+        assert (y1 - y2).abs().max().item() <= 1e-6 * yn and (y1 - y3).abs().max().item() <= 1e-6 * yn
+    else:
+        assert torch.equal(y1, y2) and torch.equal(y1, y3)
 
 
-@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split"])
+@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split", "mfma_long", "mfma_long_split"])
 def test_gate_one_keeps_state(algo):
     """f = 1: H_T = H_0 (bitwise for the fp32 kernel; within 2 ulp for the matrix-core
     kernel, which carries the state scaled by 2/ln 2) and y_t = H_0^T q_t."""
@@ -153,7 +158,7 @@ def test_deterministic(algo):
     assert np.array_equal(y1, y2) and np.array_equal(HT1, HT2)
 
 
-@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split"])
+@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split", "mfma_long", "mfma_long_split"])
 def test_chunked_continuation(algo):
     """fwd(T1) then fwd(T2, H0 = H_T) continues fwd(T1 + T2): bitwise for the fp32
     kernel, within the bf16 bar for the matrix-core kernel."""
@@ -178,7 +183,7 @@ def test_chunked_continuation(algo):
         assert nerr(HTb.cpu().numpy(), HT.cpu().numpy().astype(np.float64)) <= 1e-2
 
 
-@pytest.mark.parametrize("algo", ["mfma", "mfma_split"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_split", "mfma_long", "mfma_long_split"])
 def test_readout_self_consistency(algo):
     """y_T against H_T^T q_T recomputed in fp64 from the kernel's own H_T (the
     readout uses the state rounded to bf16 as a matrix operand)."""
@@ -200,7 +205,8 @@ def test_nondefault_stream_ordering():
     x = generate(cfg, 10)
     d = to_device(x)
     announce("non-default stream")
-    ref_y, ref_HT = m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"])
+    # bitwise comparison: the kernels with a fixed summation order
+    ref_y, ref_HT = m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], deterministic=True)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     y = torch.empty_like(ref_y)
@@ -208,7 +214,7 @@ def test_nondefault_stream_ordering():
     with torch.cuda.stream(s):
         y.fill_(float("nan"))
         HT.fill_(float("nan"))
-        m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], y=y, H_T=HT, stream=s)
+        m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], y=y, H_T=HT, stream=s, deterministic=True)
     s.synchronize()
     assert torch.equal(y, ref_y) and torch.equal(HT, ref_HT)
 
