@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "m2rnn_internal.h"
 
@@ -62,6 +63,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order
+template <typename F, int... S>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, S...>) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <int V>
@@ -130,7 +141,7 @@ struct LongStager {
         if (t < Tb) reg[p] = *reinterpret_cast<const u4*>(v + (unit * ld + t) * V + 8 * part);
       }
     }
-    freg = 0x3f80u;  // gate 1 past the end (never used: the loop stops at Tb)
+    freg = 0x3f80u;  // gate 1 past the end: the padding steps keep the state
     if (tid < kChunk && t0 + tid < Tb) freg = f[unit * ld + t0 + tid];
   }
 
@@ -378,23 +389,31 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
   lds_barrier();  // staged chunks, W-region reuse, and the operand blocks are visible
   fetch_others(NHS - 1, 1);
   f4 acc[2];
+  f4 gate = *reinterpret_cast<const f4*>(fs_all);  // step 0's gate scalars
   if (nchunks > 0) {
     rank1(0, 0, acc);
 #pragma unroll
     for (int o = 0; o < KB; ++o) products(o, acc);
   }
 
+  // Whole 16-step chunks with the step index a compile-time constant, so every
+  // LDS address of a step is a fixed offset from the chunk's bases. Steps past
+  // the sequence's end run with the staged padding (gate 1, k = v = q = 0): the
+  // blend then returns the state unchanged bit for bit, and the readout rows
+  // they produce are never added into y.
   for (int c = 0; c < nchunks; ++c) {
     const int sb = c & 1;
     const int ns = c == nchunks - 1 ? Tb - c * kChunk : kChunk;
     const float* fsb = fs_all + sb * kChunk * 4;
-    // one step; ODD steps also read out the pair (s - 1, s) and stage at s = 1.
-    // Past the sequence's last step the next step's products are still formed
-    // (from LDS contents only) and never used.
-    auto step = [&](int s, auto odd) {
-      constexpr bool ODD = decltype(odd)::value;
+    const float* fsn = fs_all + (sb ^ 1) * kChunk * 4;
+    static_for<kChunk>([&](auto si) {
+      constexpr int s = decltype(si)::value;
+      // the next step's rank-1 term goes first, into its own accumulators: it
+      // needs only staged inputs, and the matrix cores and LDS are otherwise
+      // idle during the epilogue
+      f4 accn[2];
+      if constexpr (s + 1 < kChunk) rank1(sb, s + 1, accn); else rank1(sb ^ 1, 0, accn);
       // acc holds c (G_{t-1} W + k_t v_t^T) for this wave's two tiles
-      const f4 gate = *reinterpret_cast<const f4*>(fsb + 4 * s);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -405,35 +424,28 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
         }
       make_own();
       publish_own(s & (NHS - 1), s & 1);
-      // the next step's rank-1 term and own block do not wait for the exchange
-      if (s + 1 < kChunk) rank1(sb, s + 1, acc); else rank1(sb ^ 1, 0, acc);
-      products(0, acc);
+      products(0, accn);
       lds_barrier();
+      gate = *reinterpret_cast<const f4*>((s + 1 < kChunk ? fsb : fsn) + 4 * ((s + 1) % kChunk));
       ReadoutOps ro;
-      if constexpr (ODD) ro = readout_load(sb, s - 1, 2);
+      if constexpr ((s & 1) != 0) ro = readout_load(sb, s - 1, 2);
       fetch_others(s & (NHS - 1), s & 1);
 #pragma unroll
-      for (int o = 1; o < KB; ++o) products(o, acc);
-      if constexpr (ODD) {
-        readout_mma(ro);
+      for (int o = 1; o < KB; ++o) products(o, accn);
+      acc[0] = accn[0];
+      acc[1] = accn[1];
+      if constexpr ((s & 1) != 0) readout_mma(ro);
+      if constexpr (s == 1) {
         // chunks 0 and 1 were staged before the loop; from chunk 1 on, step 1
         // stages chunk c + 1 into chunk c - 1's buffer (its last reads were
         // before this step's barrier) and fetches chunk c + 2
-        if (s == 1) {
-          if (c >= 1 && c + 1 < nchunks) {
-            st.store(lds, (c + 1) & 1);
-            if (c + 2 < nchunks) st.load(a, unit, row0, c + 2, Tb, LD);
-          }
-          add_y();  // chunk c - 1's sums
+        if (c >= 1 && c + 1 < nchunks) {
+          st.store(lds, (c + 1) & 1);
+          if (c + 2 < nchunks) st.load(a, unit, row0, c + 2, Tb, LD);
         }
+        add_y();  // chunk c - 1's sums
       }
-    };
-    for (int s = 0; s < ns; s += 2) {
-      step(s, std::false_type{});
-      if (s + 1 < ns) step(s + 1, std::true_type{});
-    }
-    if (ns & 1) readout_mma(readout_load(sb, ns - 1, 1));  // an odd-length last chunk: its final step alone
-    add_y();  // still pending only if this chunk had a single step
+    });
     Dp[0] = Dr[0];
     Dp[1] = Dr[1];
     pend_t0 = c * kChunk;
