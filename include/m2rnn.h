@@ -76,10 +76,11 @@ typedef enum m2rnn_dtype {
  *             2^-9 relative, which a sensitive trajectory can amplify.
  * MFMA_SPLIT: as MFMA with the state operand split into bf16 hi + bf16 lo and
  *             two MFMA passes (~2^-17 relative operand error).
- * AUTO:       bf16 with V in {64, 128}, T > 1 and at most 512 16-row tiles
- *             (B H K / 16 <= 512: two workgroups per CU of a 256-CU gfx950):
- *             MFMA_LONG_SPLIT; else MFMA_SPLIT where it covers the shape, else
- *             SIMPLE. With M2RNN_FLAG_DETERMINISTIC it never takes MFMA_LONG*.
+ * AUTO:       bf16 with V in {64, 128}, T > 1 and at most 768 16-row tiles
+ *             (B H K / 16 <= 768; two workgroups fit per CU of a 256-CU
+ *             gfx950): MFMA_LONG_SPLIT; else MFMA_SPLIT where it covers the
+ *             shape, else SIMPLE. With M2RNN_FLAG_DETERMINISTIC it never takes
+ *             MFMA_LONG*.
  * MFMA_LONG, MFMA_LONG_SPLIT: the same arithmetic as MFMA / MFMA_SPLIT, for
  *             workloads with few 16-row tiles (B H K / 16 well below the GPU's
  *             1024 SIMDs: small batches, long sequences). Each tile's V columns

@@ -61,10 +61,12 @@ m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const
 }
 
 m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype) {
-  // The latency-oriented kernel gives each 16-row tile a workgroup of V/32 waves;
-  // up to two such workgroups per CU of a 256-CU gfx950 it beats one wave per
-  // tile, beyond that the multi-step kernel's one wave per tile wins.
-  constexpr long double kLongMaxTiles = 512;
+  // The latency-oriented kernel gives each 16-row tile a workgroup of V/32 waves,
+  // two of which fit on a CU of a 256-CU gfx950 (LDS): up to 512 tiles run at
+  // once, and up to 768 a second partial pass still finishes before the
+  // multi-step kernel (one wave per tile, 1024 at once); beyond that the latter
+  // wins (measured at K = V = 128).
+  constexpr long double kLongMaxTiles = 768;
   if (in_dtype == M2RNN_DTYPE_BF16 && T > 1 && (V == 64 || V == 128) && supported_dim(K) &&
       (long double)B * H * (K / 16) <= kLongMaxTiles)
     return M2RNN_ALGO_MFMA_LONG_SPLIT;

@@ -127,13 +127,13 @@ def test_auto_picks_a_kernel_that_covers_the_shape():
     assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "bf16") == "mfma_split"     # 1024 row tiles
     assert m2rnn.pick_algo(1, 1, 64, 16, 16, "f32") == "simple"
     assert m2rnn.pick_algo(1, 1, 64, 16, 96, "bf16") == "simple"
-    # up to 512 16-row tiles (two workgroups per CU): the latency-oriented kernel
+    # up to 768 16-row tiles: the latency-oriented kernel
     assert m2rnn.pick_algo(1, 1, 64, 16, 128, "bf16") == "mfma_long_split"
     assert m2rnn.pick_algo(1, 32, 8192, 128, 128, "bf16") == "mfma_long_split"
     assert m2rnn.pick_algo(2, 16, 32768, 64, 128, "bf16") == "mfma_long_split"
     assert m2rnn.pick_algo(4, 8, 512, 64, 64, "bf16") == "mfma_long_split"
-    assert m2rnn.pick_algo(4, 16, 100, 128, 128, "bf16") == "mfma_long_split"  # 512 tiles
-    assert m2rnn.pick_algo(5, 16, 100, 128, 128, "bf16") == "mfma_split"       # 640 tiles
+    assert m2rnn.pick_algo(6, 16, 100, 128, 128, "bf16") == "mfma_long_split"  # 768 tiles
+    assert m2rnn.pick_algo(7, 16, 100, 128, 128, "bf16") == "mfma_split"       # 896 tiles
     assert m2rnn.pick_algo(1, 32, 1, 128, 128, "bf16") == "mfma_split"         # one step: decoding kernel
     assert m2rnn.pick_algo(1, 4, 64, 32, 64, "f32") == "simple"
     p = m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "auto")
