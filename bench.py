@@ -42,6 +42,8 @@ TRAFFIC_KIB = {
                      "1bc0c826cba1f59652c2940f5936aa56c2d4934b27d12aea700f6c8b1cf29904"),
     ("D1", "mfma"): (267823.2, 530624.2, "m2rnn_decode.hip",
                      "956ca12e91e2af7f990630af4aead6a5a4ebb04ffc1229b7d6494d0c06ac9e4f"),
+    ("C5", "mfma_long_split"): (1053889.6, 2098176.0, "m2rnn_long.hip",
+                                "41ea63a01a0c398f36aa0ffc95d09f30d205b99b89e4c35b467dcb942f29f823"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the
