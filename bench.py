@@ -218,7 +218,13 @@ def train_bench(args, cfg, dev, x):
     dy = torch.randn((B, H, T, V), dtype=torch.float32, device="cuda", generator=g)
     y = torch.empty((B, H, T, V), dtype=torch.float32, device="cuda")
     HT = torch.empty((B, H, K, V), dtype=torch.float32, device="cuda")
-    algo = args.algo if args.algo not in (None, "mfma") else "mfma_split"
+    # default: the library's choice for training (the split operand; on the
+    # latency-oriented kernel for few row tiles)
+    if args.algo in (None, "auto"):
+        picked = m2rnn.pick_algo(B, H, T, K, V, cfg.dtype)
+        algo = picked if picked == "mfma_long_split" else "mfma_split"
+    else:
+        algo = args.algo
     k, v, q, f, W, H0 = (dev[n] for n in ("k", "v", "q", "f", "W", "H0"))
 
     def timed(fwd, bwd):

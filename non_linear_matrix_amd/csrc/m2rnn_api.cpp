@@ -51,6 +51,35 @@ m2rnn_status check(const void* k, const void* v, const void* q, const void* f, c
 
 }  // namespace
 
+extern "C" m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype);
+
+namespace {
+
+// The training entry points' forward kernel: AUTO takes the split operand, on
+// the latency-oriented kernel where m2rnn_pick_algo would; explicit families
+// are the four matrix-core ones, on the shapes the backward pass covers.
+m2rnn_status training_algo(m2rnn_algo& algo, int B, int H, int T, int K, int V, m2rnn_dtype dt) {
+  if (algo == M2RNN_ALGO_AUTO) {
+    algo = m2rnn_pick_algo(B, H, T, K, V, dt);
+    if (algo != M2RNN_ALGO_MFMA_LONG_SPLIT) algo = M2RNN_ALGO_MFMA_SPLIT;
+  }
+  switch (algo) {
+    case M2RNN_ALGO_MFMA:
+    case M2RNN_ALGO_MFMA_SPLIT:
+      return M2RNN_SUCCESS;
+    case M2RNN_ALGO_MFMA_LONG:
+    case M2RNN_ALGO_MFMA_LONG_SPLIT:
+      return m2rnn::mfma_supports(K, V, dt == M2RNN_DTYPE_BF16) ? M2RNN_SUCCESS : M2RNN_ERROR_NOT_SUPPORTED;
+    default:
+      return M2RNN_ERROR_NOT_SUPPORTED;
+  }
+}
+
+bool is_long(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT; }
+bool is_split(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_SPLIT || algo == M2RNN_ALGO_MFMA_LONG_SPLIT; }
+
+}  // namespace
+
 extern "C" {
 
 m2rnn_status m2rnn_check_args(const void* k, const void* v, const void* q, const void* f,
@@ -138,13 +167,14 @@ m2rnn_status m2rnn_fwd_save(const void* k, const void* v, const void* q, const v
                             const void* W, const float* H0, float* y, float* H_T, void* saved,
                             int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                             m2rnn_algo algo, void* stream) {
-  if (algo == M2RNN_ALGO_AUTO) algo = M2RNN_ALGO_MFMA_SPLIT;
-  if (algo != M2RNN_ALGO_MFMA && algo != M2RNN_ALGO_MFMA_SPLIT) return M2RNN_ERROR_NOT_SUPPORTED;
   m2rnn_status st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
+  if ((st = training_algo(algo, B, H, T, K, V, in_dtype)) != M2RNN_SUCCESS) return st;
+  if ((st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo)) != M2RNN_SUCCESS) return st;
   if (!saved || !aligned16(saved)) return M2RNN_ERROR_INVALID_VALUE;
   m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, 1, 0, nullptr, saved};
-  hipError_t e = m2rnn::launch_mfma(a, algo == M2RNN_ALGO_MFMA_SPLIT, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = is_long(algo) ? m2rnn::launch_long(a, is_split(algo), s) : m2rnn::launch_mfma(a, is_split(algo), s);
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
 }
 
@@ -179,15 +209,15 @@ m2rnn_status m2rnn_fwd_ckpt(const void* k, const void* v, const void* q, const v
                             const void* W, const float* H0, float* y, float* H_T, float* ckpt,
                             int B, int H, int T, int K, int V, int segment, m2rnn_dtype in_dtype,
                             m2rnn_algo algo, void* stream) {
-  if (algo == M2RNN_ALGO_AUTO) algo = M2RNN_ALGO_MFMA_SPLIT;
-  if (algo != M2RNN_ALGO_MFMA && algo != M2RNN_ALGO_MFMA_SPLIT) return M2RNN_ERROR_NOT_SUPPORTED;
   m2rnn_status st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
+  if ((st = training_algo(algo, B, H, T, K, V, in_dtype)) != M2RNN_SUCCESS) return st;
+  if ((st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo)) != M2RNN_SUCCESS) return st;
   if (segment < 1) return M2RNN_ERROR_INVALID_VALUE;
   if (m2rnn::ckpt_bytes(B, H, T, K, V, segment) > 0 && (!ckpt || !aligned16(ckpt)))
     return M2RNN_ERROR_INVALID_VALUE;
   m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, 1, 0, nullptr, nullptr, 0};
-  hipError_t e = m2rnn::launch_fwd_ckpt(a, ckpt, segment, algo == M2RNN_ALGO_MFMA_SPLIT,
+  hipError_t e = m2rnn::launch_fwd_ckpt(a, ckpt, segment, is_split(algo), is_long(algo),
                                         reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
 }
@@ -204,10 +234,10 @@ m2rnn_status m2rnn_bwd_recompute(const void* k, const void* v, const void* q, co
                                  float* dW, float* dH0, void* workspace, int B, int H, int T, int K,
                                  int V, int segment, m2rnn_dtype in_dtype, m2rnn_algo algo,
                                  void* stream) {
-  if (algo == M2RNN_ALGO_AUTO) algo = M2RNN_ALGO_MFMA_SPLIT;
-  if (algo != M2RNN_ALGO_MFMA && algo != M2RNN_ALGO_MFMA_SPLIT) return M2RNN_ERROR_NOT_SUPPORTED;
   m2rnn_status st = check(k, v, q, f, W, H0, dy, dH_T, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
+  if ((st = training_algo(algo, B, H, T, K, V, in_dtype)) != M2RNN_SUCCESS) return st;
+  if ((st = check(k, v, q, f, W, H0, dy, dH_T, B, H, T, K, V, in_dtype, algo)) != M2RNN_SUCCESS) return st;
   if (segment < 1 || !dk || !dv || !dq || !df || !dW || !workspace) return M2RNN_ERROR_INVALID_VALUE;
   if (m2rnn::ckpt_bytes(B, H, T, K, V, segment) > 0 && (!ckpt || !aligned16(ckpt)))
     return M2RNN_ERROR_INVALID_VALUE;
@@ -216,7 +246,7 @@ m2rnn_status m2rnn_bwd_recompute(const void* k, const void* v, const void* q, co
     return M2RNN_ERROR_INVALID_VALUE;
   m2rnn::BwdLaunch p{k, v, q, f, W, nullptr, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V,
                      0, 0, 0};
-  hipError_t e = m2rnn::launch_bwd_recompute(p, H0, ckpt, segment, algo == M2RNN_ALGO_MFMA_SPLIT,
+  hipError_t e = m2rnn::launch_bwd_recompute(p, H0, ckpt, segment, is_split(algo), is_long(algo),
                                              reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
 }

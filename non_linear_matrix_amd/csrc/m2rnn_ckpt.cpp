@@ -38,11 +38,14 @@ long long bwd_recompute_workspace_bytes(int B, int H, int T, int K, int V, int S
          2 * round256((long long)B * H * K * V * 4);
 }
 
-hipError_t launch_fwd_ckpt(const FwdArgs& a, float* ckpt, int S, bool split, hipStream_t stream) {
+hipError_t launch_fwd_ckpt(const FwdArgs& a, float* ckpt, int S, bool split, bool lng, hipStream_t stream) {
   const int nseg = nsegments(a.T, S);
-  const Plan pl = plan_mfma(a.B, a.H, a.K, a.V, split);
-  if (pl.grid < 0) return hipErrorInvalidValue;
-  const bool add = pl.groups_per_unit > 1;  // two workgroups add their readouts into y
+  bool add = true;  // the latency-oriented kernel's row tiles add their readouts into y
+  if (!lng) {
+    const Plan pl = plan_mfma(a.B, a.H, a.K, a.V, split);
+    if (pl.grid < 0) return hipErrorInvalidValue;
+    add = pl.groups_per_unit > 1;  // two workgroups add their readouts into y
+  }
   hipError_t e;
   if (add && (e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream)) != hipSuccess) return e;
   const long long unitKV = (long long)a.B * a.H * a.K * a.V;
@@ -61,13 +64,13 @@ hipError_t launch_fwd_ckpt(const FwdArgs& a, float* ckpt, int S, bool split, hip
     w.HT = j == nseg - 1 ? a.HT : ckpt + j * unitKV;
     w.lens = nullptr;
     w.saved = nullptr;
-    if ((e = launch_mfma(w, split, stream)) != hipSuccess) return e;
+    if ((e = lng ? launch_long(w, split, stream) : launch_mfma(w, split, stream)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_bwd_recompute(const BwdLaunch& p, const float* H0, const float* ckpt, int S, bool split,
-                                hipStream_t stream) {
+                                bool lng, hipStream_t stream) {
   const int nseg = nsegments(p.T, S);
   const int Sw = S < p.T ? S : p.T;
   char* ws = static_cast<char*>(p.workspace);
@@ -93,7 +96,7 @@ hipError_t launch_bwd_recompute(const BwdLaunch& p, const float* H0, const float
     // 1. the segment's states and pre-activations, from its checkpoint
     FwdArgs fa{k, v, q, f, p.W, j == 0 ? H0 : ckpt + (j - 1) * unitKV, nullptr, nullptr,
                p.B, p.H, Tj, p.K, p.V, 1, 0, nullptr, saved, p.T};
-    if ((e = launch_mfma(fa, split, stream)) != hipSuccess) return e;
+    if ((e = lng ? launch_long(fa, split, stream) : launch_mfma(fa, split, stream)) != hipSuccess) return e;
     // 2. reverse time over the segment, then its share of dW
     float* dH_out = j == 0 ? p.dH0 : carry[j & 1];
     BwdLaunch b{k, v, q, f, p.W, saved, p.dy + t0 * p.V, dH_in,

@@ -79,11 +79,12 @@ long long bwd_workspace_bytes(int B, int H, int T, int K, int V);
 long long ckpt_bytes(int B, int H, int T, int K, int V, int S);
 long long bwd_recompute_workspace_bytes(int B, int H, int T, int K, int V, int S);
 // a.saved, a.lens and a.ld are ignored; ckpt receives the states at steps S, 2S, ...
-hipError_t launch_fwd_ckpt(const FwdArgs& a, float* ckpt, int S, bool split, hipStream_t stream);
+// lng / split pick the forward kernel (latency-oriented or multi-step, split operand)
+hipError_t launch_fwd_ckpt(const FwdArgs& a, float* ckpt, int S, bool split, bool lng, hipStream_t stream);
 // p.saved, p.ld and the flags are ignored; p.workspace holds
-// bwd_recompute_workspace_bytes; split picks the forward that recomputes the states
+// bwd_recompute_workspace_bytes; lng / split pick the forward that recomputes the states
 hipError_t launch_bwd_recompute(const BwdLaunch& p, const float* H0, const float* ckpt, int S, bool split,
-                                hipStream_t stream);
+                                bool lng, hipStream_t stream);
 
 // Layer front-end (m2rnn_frontend.hip): k, v, q and f from x (bf16).
 struct FrontLaunch {

@@ -192,7 +192,7 @@ struct LongStager {
   }
 };
 
-template <int V, bool SPLIT>
+template <int V, bool SPLIT, bool SAVE>
 __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kernel(FwdArgs a) {
   using L = LongLayout<V>;
   constexpr int KB = V / 32, HROW = L::HROW, NHS = L::NHS;
@@ -383,8 +383,15 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
     pend_n = 0;
   };
 
+  // training forward: the multi-step kernel's saved layout (per step, 1 KB per
+  // row tile and 32-column block, lane l's 16 bytes at 16 l); this wave's block
+  // is w
+  [[maybe_unused]] char* const saved = static_cast<char*>(a.saved);
+  [[maybe_unused]] const long long sv_off = (long long)(row0 / 16) * (V / 32) * 1024 + w * 1024 + l * 16;
+
   // initial operand: every wave's block of G_0 through the shared tile (slot NHS - 1)
   make_own();
+  if constexpr (SAVE) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, 0, T, a.K, V) + sv_off) = Bf[0];
   publish_own(NHS - 1, 1);
   lds_barrier();  // staged chunks, W-region reuse, and the operand blocks are visible
   fetch_others(NHS - 1, 1);
@@ -414,6 +421,13 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
       f4 accn[2];
       if constexpr (s + 1 < kChunk) rank1(sb, s + 1, accn); else rank1(sb ^ 1, 0, accn);
       // acc holds c (G_{t-1} W + k_t v_t^T) for this wave's two tiles
+      [[maybe_unused]] const int t = c * kChunk + s;
+      if constexpr (SAVE) {
+        if (t < Tb)
+          *reinterpret_cast<u4*>(saved + saved_pre_off(unit, t, a.B, a.H, T, a.K, V) + sv_off) =
+              u4{pack_bf16(acc[0][0], acc[0][1]), pack_bf16(acc[0][2], acc[0][3]), pack_bf16(acc[1][0], acc[1][1]),
+                 pack_bf16(acc[1][2], acc[1][3])};
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -423,6 +437,9 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
           G[j][i] = fmaf(gate[2], r, fmaf(gate[0], G[j][i], gate[1]));
         }
       make_own();
+      if constexpr (SAVE) {
+        if (t < Tb) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, t + 1, T, a.K, V) + sv_off) = Bf[0];
+      }
       publish_own(s & (NHS - 1), s & 1);
       products(0, accn);
       lds_barrier();
@@ -469,7 +486,7 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
 }  // namespace
 
 bool long_supports(const FwdArgs& a) {
-  return a.bf16 && a.saved == nullptr && (a.V == 64 || a.V == 128) && a.K % 16 == 0 && a.K >= 16 && a.K <= 128;
+  return a.bf16 && (a.V == 64 || a.V == 128) && a.K % 16 == 0 && a.K >= 16 && a.K <= 128;
 }
 
 Plan plan_long(int B, int H, int K, int V) {
@@ -487,18 +504,23 @@ hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream) {
     hipError_t e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream);
     if (e != hipSuccess) return e;
   }
-  const dim3 block(64 * (a.V / 32));
+  const dim3 block(64 * (a.V / 32)), gr((unsigned)grid);
+  const bool save = a.saved != nullptr;
+#define M2RNN_LONG_LAUNCH(V_, S_, SV_) hipLaunchKernelGGL((mfma_fwd_long_kernel<V_, S_, SV_>), gr, block, 0, stream, a)
   if (a.V == 128) {
-    if (split)
-      hipLaunchKernelGGL((mfma_fwd_long_kernel<128, true>), dim3((unsigned)grid), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mfma_fwd_long_kernel<128, false>), dim3((unsigned)grid), block, 0, stream, a);
+    if (split) {
+      if (save) M2RNN_LONG_LAUNCH(128, true, true); else M2RNN_LONG_LAUNCH(128, true, false);
+    } else {
+      if (save) M2RNN_LONG_LAUNCH(128, false, true); else M2RNN_LONG_LAUNCH(128, false, false);
+    }
   } else {
-    if (split)
-      hipLaunchKernelGGL((mfma_fwd_long_kernel<64, true>), dim3((unsigned)grid), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mfma_fwd_long_kernel<64, false>), dim3((unsigned)grid), block, 0, stream, a);
+    if (split) {
+      if (save) M2RNN_LONG_LAUNCH(64, true, true); else M2RNN_LONG_LAUNCH(64, true, false);
+    } else {
+      if (save) M2RNN_LONG_LAUNCH(64, false, true); else M2RNN_LONG_LAUNCH(64, false, false);
+    }
   }
+#undef M2RNN_LONG_LAUNCH
   return hipGetLastError();
 }
 

@@ -212,6 +212,27 @@ def test_recompute_entry_points_validate_before_launching():
     assert bwd(p, 16, algo=simple) == UNSUPPORTED
 
 
+def test_training_forwards_take_the_long_kernel_only_where_the_backward_covers_the_shape():
+    """The saving forwards accept MFMA_LONG* (same saved layout), but not for a
+    shape the backward pass does not cover (K = 16, V = 96) nor in fp32; all
+    refused before any launch."""
+    lib = m2rnn.load()
+    p = 0x10000
+    bf16, f32 = m2rnn.DTYPES["bf16"], m2rnn.DTYPES["f32"]
+    for algo in ("mfma_long", "mfma_long_split"):
+        a = m2rnn.ALGOS[algo]
+        save = lambda K, V, dt=bf16: lib.m2rnn_fwd_save(p, p, p, p, p, None, p, None, p, 2, 2, 16, K, V, dt, a, None)
+        assert save(16, 64) == UNSUPPORTED, algo
+        assert save(64, 96) == UNSUPPORTED, algo
+        assert save(64, 64, f32) == UNSUPPORTED, algo
+        ck = lambda K: lib.m2rnn_fwd_ckpt(p, p, p, p, p, None, p, None, p, 2, 2, 64, K, 64, 16, bf16, a, None)
+        assert ck(16) == UNSUPPORTED, algo
+        rc = lambda K: lib.m2rnn_bwd_recompute(p, p, p, p, p, None, p, p, None, p, p, p, p, p, None, p,
+                                               2, 2, 64, K, 64, 16, bf16, a, None)
+        assert rc(16) == UNSUPPORTED, algo
+        assert lib.m2rnn_fwd_save(None, p, p, p, p, None, p, None, p, 2, 2, 16, 64, 64, bf16, a, None) == INVALID
+
+
 def test_frontend_validates_before_launching():
     lib = m2rnn.load()
     p = 0x10000

@@ -130,10 +130,10 @@ def test_plan_and_training_entry_points():
     q = m2rnn.get_plan(2, 16, 32768, 64, 128, "bf16", "mfma_long_split")
     assert q["grid"] == 32 * 4
     lib = m2rnn.load()
-    pt = 0x10000
-    st = lib.m2rnn_fwd_save(pt, pt, pt, pt, pt, None, pt, None, pt, 2, 2, 16, 64, 64, m2rnn.DTYPES["bf16"],
+    pt = 0x10000  # never dereferenced: the call is refused before any launch
+    st = lib.m2rnn_fwd_save(pt, pt, pt, pt, pt, None, pt, None, pt, 2, 2, 16, 16, 64, m2rnn.DTYPES["bf16"],
                             m2rnn.ALGOS["mfma_long"], None)
-    assert st == 2  # NOT_SUPPORTED, before any launch
+    assert st == 2  # NOT_SUPPORTED: K = 16 has no backward pass
 
 
 def test_auto_takes_the_long_kernel_unless_deterministic():
@@ -188,3 +188,54 @@ def test_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(HT, HT_e), r
         assert (y - y_e).abs().max().item() <= 1e-6 * y_e.abs().max().item(), r
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_training_forward_feeds_the_backward(split):
+    """The saving forward on the latency-oriented kernel writes the multi-step
+    kernel's saved layout: the backward takes either, the gradients agree to the
+    fp32 summation order of the states (and both match the oracle)."""
+    import torch
+    from non_linear_matrix_amd import m2rnn
+    from oracle import m2rnn_bwd_ref
+
+    cfg = scaled(CONFIGS["C3"], B=2, H=2, K=64, T=45)
+    announce(f"long saving forward, split={split}")
+    x = generate(cfg, 68)
+    d = to_device(x)
+    dy = torch.randn((cfg.B, cfg.H, cfg.T, cfg.V), generator=torch.Generator().manual_seed(8)).cuda()
+    grads, outs = [], []
+    for algo in (("mfma_long_split", "mfma_split") if split else ("mfma_long", "mfma")):
+        y, HT, saved = m2rnn.fwd_save(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], algo=algo)
+        grads.append(m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, dy))
+        outs.append((y, HT))
+    torch.cuda.synchronize()
+    assert nerr(outs[0][1].cpu().numpy(), outs[1][1].cpu().numpy().astype(np.float64)) <= (1e-4 if split else 4e-3)
+    assert nerr(outs[0][0].cpu().numpy(), outs[1][0].cpu().numpy().astype(np.float64)) <= 2.0 ** -8
+    ref = m2rnn_bwd_ref(x["k"], x["v"], x["q"], x["f"], x["W"], x["H0"], dy.cpu().numpy(), dtype=cfg.dtype)
+    for key in ("dk", "dv", "dq", "df", "dW", "dH0"):
+        a, b = grads[0][key].cpu().numpy(), grads[1][key].cpu().numpy()
+        assert nerr(a, b.astype(np.float64)) <= (1e-3 if split else 1e-2), key
+        assert nerr(a, ref[key]) <= TOL, key
+
+
+def test_recompute_mode_on_the_long_kernel():
+    """Checkpointing forward and recomputing backward with the latency-oriented
+    forward, several segments, against the oracle."""
+    import torch
+    from non_linear_matrix_amd import m2rnn
+    from oracle import m2rnn_bwd_ref
+
+    cfg = scaled(CONFIGS["C5"], B=2, H=2, T=70)
+    announce("long kernel recompute mode, segments of 16")
+    x = generate(cfg, 69)
+    d = to_device(x)
+    dy = torch.randn((cfg.B, cfg.H, cfg.T, cfg.V), generator=torch.Generator().manual_seed(9)).cuda()
+    y, HT, ck = m2rnn.fwd_ckpt(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], segment=16, algo="mfma_long_split")
+    g = m2rnn.bwd_recompute(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], ck, dy, segment=16,
+                            algo="mfma_long_split")
+    torch.cuda.synchronize()
+    ref = m2rnn_bwd_ref(x["k"], x["v"], x["q"], x["f"], x["W"], x["H0"], dy.cpu().numpy(), dtype=cfg.dtype)
+    assert nerr(y.cpu().numpy(), ref["y"]) <= TOL and nerr(HT.cpu().numpy(), ref["H_T"]) <= TOL
+    for key in ("dk", "dv", "dq", "df", "dW", "dH0"):
+        assert nerr(g[key].cpu().numpy(), ref[key]) <= TOL, key

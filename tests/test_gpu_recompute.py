@@ -115,7 +115,10 @@ def test_one_segment_equals_the_saved_state_backward_bit_for_bit():
     g2 = m2rnn.bwd_recompute(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], ck, dyt, dHTt, segment=cfg.T)
     torch.cuda.synchronize()
     assert ck is None
-    assert torch.equal(y1, y2) and torch.equal(H1, H2)
+    assert torch.equal(H1, H2)
+    # y: the latency-oriented forward (AUTO here) sums it over row tiles with
+    # atomic adds, so only to rounding
+    assert (y1 - y2).abs().max().item() <= 1e-6 * y1.abs().max().item()
     for key in GRADS:
         assert torch.equal(g1[key], g2[key]), key
 
