@@ -88,8 +88,9 @@ typedef enum m2rnn_dtype {
  *             LDS every step, which cuts the per-step latency; each tile is its
  *             own workgroup, so y is summed over a unit's K/16 tiles with atomic
  *             adds whose order, and hence y's last bits, can vary between runs
- *             (H_T cannot). bf16, K in {16, ..., 128}, V in {64, 128}; forward
- *             entry points only (the training ones return NOT_SUPPORTED). */
+ *             (H_T cannot). bf16, K in {16, ..., 128}, V in {64, 128}; the
+ *             training forwards take them for K in {32, 64, 128} (the shapes
+ *             the backward pass covers) and write the same `saved` layout. */
 typedef enum m2rnn_algo {
   M2RNN_ALGO_AUTO = 0,
   M2RNN_ALGO_SIMPLE = 1,
@@ -161,9 +162,11 @@ m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const
  * ((2T + 1) * B * H * K * V * 2; 0 when the shape is not covered). */
 unsigned long long m2rnn_saved_bytes(int B, int H, int T, int K, int V);
 
-/* m2rnn_fwd_algo (algo AUTO, MFMA or MFMA_SPLIT) that also fills `saved`
- * (device, 16-byte aligned, m2rnn_saved_bytes large, caller-owned; its layout
- * is private to the library and only m2rnn_bwd reads it). */
+/* Training forward: m2rnn_fwd_algo that also fills `saved` (device, 16-byte
+ * aligned, m2rnn_saved_bytes large, caller-owned; its layout is private to the
+ * library and only m2rnn_bwd reads it). algo: MFMA, MFMA_SPLIT, MFMA_LONG,
+ * MFMA_LONG_SPLIT (the same layout), or AUTO = the split operand, on
+ * MFMA_LONG_SPLIT where m2rnn_pick_algo would take it, else MFMA_SPLIT. */
 m2rnn_status m2rnn_fwd_save(const void* k, const void* v, const void* q, const void* f, const void* W,
                             const float* H0, float* y, float* H_T, void* saved,
                             int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
@@ -202,7 +205,7 @@ m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* 
  * (0: none needed, or invalid sizes). */
 unsigned long long m2rnn_ckpt_bytes(int B, int H, int T, int K, int V, int segment);
 
-/* m2rnn_fwd_algo (algo AUTO = MFMA_SPLIT, MFMA or MFMA_SPLIT) that also writes
+/* m2rnn_fwd_algo (algo as m2rnn_fwd_save) that also writes
  * ckpt[j - 1] = H_{j * segment} for j = 1 .. ceil(T/segment) - 1, fp32
  * [B][H][K][V] each (device, 16-byte aligned, caller-owned; may be NULL when
  * m2rnn_ckpt_bytes is 0). It runs as one launch per segment.
@@ -217,9 +220,9 @@ unsigned long long m2rnn_bwd_recompute_workspace_bytes(int B, int H, int T, int 
 
 /* Backward pass from checkpoints: arguments as m2rnn_bwd, with `ckpt` from
  * m2rnn_fwd_ckpt (same inputs, same segment) in place of `saved`, and H0 the
- * initial state of the forward call (NULL: zero). `algo` (AUTO = MFMA_SPLIT)
- * must be the one the forward pass ran, so that the recomputed states are the
- * ones that produced y. `workspace`: m2rnn_bwd_recompute_workspace_bytes large.
+ * initial state of the forward call (NULL: zero). `algo` (as m2rnn_fwd_save)
+ * should be the one the forward pass ran, so that the recomputed states are
+ * the ones that produced y (another family rebuilds them to fp32 rounding). `workspace`: m2rnn_bwd_recompute_workspace_bytes large.
  * Issues five to seven launches per segment on `stream`. */
 m2rnn_status m2rnn_bwd_recompute(const void* k, const void* v, const void* q, const void* f,
                                  const void* W, const float* H0, const float* ckpt, const float* dy,
@@ -285,7 +288,8 @@ const char* m2rnn_status_string(m2rnn_status status);
 
 /* Library ABI version: major * 10000 + minor * 100 + patch (0.2.0 added
  * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones and the front-end, 0.4.0 MFMA_LONG, 0.5.0 AUTO's
- * choice of MFMA_LONG_SPLIT and M2RNN_FLAG_DETERMINISTIC). */
+ * choice of MFMA_LONG_SPLIT and M2RNN_FLAG_DETERMINISTIC, 0.6.0 MFMA_LONG* in
+ * the training forwards). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

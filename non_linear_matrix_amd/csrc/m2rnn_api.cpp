@@ -313,6 +313,6 @@ const char* m2rnn_status_string(m2rnn_status status) {
   }
 }
 
-int m2rnn_version(void) { return 500; }
+int m2rnn_version(void) { return 600; }
 
 }  // extern "C"
