@@ -189,6 +189,19 @@ m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* 
                        void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                        void* stream);
 
+/* m2rnn_bwd with an explicit reverse-time kernel (m2rnn_bwd is AUTO). MFMA,
+ * MFMA_SPLIT: one wave per 16-row tile; MFMA_LONG, MFMA_LONG_SPLIT: a workgroup
+ * of V/32 waves per tile exchanging dA through LDS every step (few tiles, long
+ * sequences), its dv and df sums over a unit's tiles added in tile order by a
+ * second kernel; AUTO: MFMA_LONG_SPLIT where m2rnn_pick_algo would take it.
+ * Either kernel reads the `saved` of either forward family, and every output is
+ * deterministic. NOT_SUPPORTED for other families. */
+m2rnn_status m2rnn_bwd_algo(const void* k, const void* v, const void* q, const void* f, const void* W,
+                            const float* H0, const void* saved, const float* dy, const float* dH_T,
+                            float* dk, float* dv, float* dq, float* df, float* dW, float* dH0,
+                            void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, void* stream);
+
 /* ---- Training with recomputation (zh summary §2.2, parallelism paragraph: the
  * backward pass recomputes the forward states rather than keeping them all).
  * The sequence is cut into segments of `segment` steps (the last one may be
@@ -221,8 +234,10 @@ unsigned long long m2rnn_bwd_recompute_workspace_bytes(int B, int H, int T, int 
 /* Backward pass from checkpoints: arguments as m2rnn_bwd, with `ckpt` from
  * m2rnn_fwd_ckpt (same inputs, same segment) in place of `saved`, and H0 the
  * initial state of the forward call (NULL: zero). `algo` (as m2rnn_fwd_save)
- * should be the one the forward pass ran, so that the recomputed states are
- * the ones that produced y (another family rebuilds them to fp32 rounding). `workspace`: m2rnn_bwd_recompute_workspace_bytes large.
+ * picks the forward that recomputes the states and the reverse kernel (as
+ * m2rnn_bwd_algo); it should be the one the forward pass ran, so that the
+ * recomputed states are the ones that produced y (another family rebuilds them
+ * to fp32 rounding). `workspace`: m2rnn_bwd_recompute_workspace_bytes large.
  * Issues five to seven launches per segment on `stream`. */
 m2rnn_status m2rnn_bwd_recompute(const void* k, const void* v, const void* q, const void* f,
                                  const void* W, const float* H0, const float* ckpt, const float* dy,
@@ -289,7 +304,7 @@ const char* m2rnn_status_string(m2rnn_status status);
 /* Library ABI version: major * 10000 + minor * 100 + patch (0.2.0 added
  * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones and the front-end, 0.4.0 MFMA_LONG, 0.5.0 AUTO's
  * choice of MFMA_LONG_SPLIT and M2RNN_FLAG_DETERMINISTIC, 0.6.0 MFMA_LONG* in
- * the training forwards). */
+ * the training forwards and m2rnn_bwd_algo). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libm2rnn.so")
-SOURCES = ["m2rnn_api.cpp", "m2rnn_simple.hip", "m2rnn_mfma.hip", "m2rnn_bwd.hip", "m2rnn_ckpt.cpp", "m2rnn_frontend.hip", "m2rnn_decode.hip", "m2rnn_long.hip"]
+SOURCES = ["m2rnn_api.cpp", "m2rnn_simple.hip", "m2rnn_mfma.hip", "m2rnn_bwd.hip", "m2rnn_ckpt.cpp", "m2rnn_frontend.hip", "m2rnn_decode.hip", "m2rnn_long.hip", "m2rnn_bwd_long.hip"]
 ARCH = "gfx950"
 
 

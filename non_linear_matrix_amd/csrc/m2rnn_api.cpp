@@ -183,21 +183,32 @@ unsigned long long m2rnn_bwd_workspace_bytes(int B, int H, int T, int K, int V) 
   return static_cast<unsigned long long>(m2rnn::bwd_workspace_bytes(B, H, T, K, V));
 }
 
+m2rnn_status m2rnn_bwd_algo(const void* k, const void* v, const void* q, const void* f, const void* W,
+                            const float* H0, const void* saved, const float* dy, const float* dH_T,
+                            float* dk, float* dv, float* dq, float* df, float* dW, float* dH0,
+                            void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, void* stream) {
+  // the forward's argument rules, with dy standing in for y
+  m2rnn_status st = check(k, v, q, f, W, H0, dy, dH_T, B, H, T, K, V, in_dtype, M2RNN_ALGO_MFMA);
+  if (st != M2RNN_SUCCESS) return st;
+  if ((st = training_algo(algo, B, H, T, K, V, in_dtype)) != M2RNN_SUCCESS) return st;
+  if (!saved || !dk || !dv || !dq || !df || !dW || !workspace) return M2RNN_ERROR_INVALID_VALUE;
+  if (!aligned16(saved) || !aligned16(dk) || !aligned16(dv) || !aligned16(dq) || !aligned16(df) ||
+      !aligned16(dW) || !aligned16(workspace) || (dH0 && !aligned16(dH0)))
+    return M2RNN_ERROR_INVALID_VALUE;
+  m2rnn::BwdLaunch p{k, v, q, f, W, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V,
+                     0, 0, 0, is_long(algo) ? 1 : 0};
+  hipError_t e = m2rnn::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+}
+
 m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* f, const void* W,
                        const float* H0, const void* saved, const float* dy, const float* dH_T,
                        float* dk, float* dv, float* dq, float* df, float* dW, float* dH0,
                        void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                        void* stream) {
-  // the forward's argument rules, with dy standing in for y
-  m2rnn_status st = check(k, v, q, f, W, H0, dy, dH_T, B, H, T, K, V, in_dtype, M2RNN_ALGO_MFMA);
-  if (st != M2RNN_SUCCESS) return st;
-  if (!saved || !dk || !dv || !dq || !df || !dW || !workspace) return M2RNN_ERROR_INVALID_VALUE;
-  if (!aligned16(saved) || !aligned16(dk) || !aligned16(dv) || !aligned16(dq) || !aligned16(df) ||
-      !aligned16(dW) || !aligned16(workspace) || (dH0 && !aligned16(dH0)))
-    return M2RNN_ERROR_INVALID_VALUE;
-  m2rnn::BwdLaunch p{k, v, q, f, W, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V};
-  hipError_t e = m2rnn::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+  return m2rnn_bwd_algo(k, v, q, f, W, H0, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V,
+                        in_dtype, M2RNN_ALGO_AUTO, stream);
 }
 
 unsigned long long m2rnn_ckpt_bytes(int B, int H, int T, int K, int V, int segment) {

@@ -521,6 +521,20 @@ int dw_splits(int B, int T, int K) {
   return static_cast<int>(s);
 }
 
+// dW from the saved states and the reverse kernel's dA slots
+template <int V>
+hipError_t launch_dw(const BwdArgs& a, float* partial, float* dW, bool dW_acc, hipStream_t stream) {
+  hipError_t e;
+  const int ns = dw_splits(a.B, a.T, a.K);
+  hipLaunchKernelGGL((dw_partial_kernel<V>), dim3((unsigned)(a.H * ns)), dim3(256), 0, stream, a.saved, a.dA_out,
+                     partial, a.B, a.H, a.T, a.K, ns);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long long nel = (long long)a.H * V * V;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, stream, partial, dW, a.H,
+                     V * V, ns, dW_acc ? 1 : 0);
+  return hipGetLastError();
+}
+
 template <int V, int NW>
 hipError_t launch_bwd_t(const BwdArgs& a, float* partial, float* dW, bool zeroed, bool dW_acc,
                         hipStream_t stream) {
@@ -536,20 +550,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* partial, float* dW, bool zeroed
   }
   hipLaunchKernelGGL((mfma_bwd_kernel<V, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int ns = dw_splits(a.B, a.T, a.K);
-  hipLaunchKernelGGL((dw_partial_kernel<V>), dim3((unsigned)(a.H * ns)), dim3(256), 0, stream, a.saved, a.dA_out,
-                     partial, a.B, a.H, a.T, a.K, ns);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long long nel = (long long)a.H * V * V;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0, stream, partial, dW, a.H,
-                     V * V, ns, dW_acc ? 1 : 0);
-  return hipGetLastError();
+  return launch_dw<V>(a, partial, dW, dW_acc, stream);
 }
 
 }  // namespace
 
 long long bwd_workspace_bytes(int B, int H, int T, int K, int V) {
-  return (long long)B * H * T * saved_slot_bytes(K, V) + (long long)H * dw_splits(B, T, K) * V * V * 4;
+  return (long long)B * H * T * saved_slot_bytes(K, V) + (long long)H * dw_splits(B, T, K) * V * V * 4 +
+         ((V == 64 || V == 128) ? bwd_long_partial_bytes(B, H, T, K, V) : 0);
 }
 
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream) {
@@ -561,6 +569,12 @@ hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream) {
   const bool z = p.dvdf_zeroed != 0, acc = p.dW_accumulate != 0;
   float* partial = reinterpret_cast<float*>(static_cast<char*>(p.workspace) +
                                             (long long)p.B * p.H * p.T * saved_slot_bytes(p.K, p.V));
+  if (p.long_kernel) {
+    float* lp = partial + (long long)p.H * dw_splits(p.B, p.T, p.K) * p.V * p.V;
+    hipError_t e = launch_bwd_long(p, static_cast<char*>(p.workspace), lp, stream);
+    if (e != hipSuccess) return e;
+    return p.V == 128 ? launch_dw<128>(a, partial, p.dW, acc, stream) : launch_dw<64>(a, partial, p.dW, acc, stream);
+  }
   const int nw = p.K % 64 == 0 && p.K / 64 <= 2 ? 4 : (p.K % 32 == 0 && p.K / 32 <= 2 ? 2 : 0);
   if (p.V == 128)
     return nw == 4 ? launch_bwd_t<128, 4>(a, partial, p.dW, z, acc, stream)

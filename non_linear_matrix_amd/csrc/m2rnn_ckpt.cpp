@@ -101,7 +101,7 @@ hipError_t launch_bwd_recompute(const BwdLaunch& p, const float* H0, const float
     float* dH_out = j == 0 ? p.dH0 : carry[j & 1];
     BwdLaunch b{k, v, q, f, p.W, saved, p.dy + t0 * p.V, dH_in,
                 p.dk + t0 * p.K, p.dv + t0 * p.V, p.dq + t0 * p.K, p.df + t0, p.dW, dH_out, bws,
-                p.B, p.H, Tj, p.K, p.V, p.T, 1, j == nseg - 1 ? 0 : 1};
+                p.B, p.H, Tj, p.K, p.V, p.T, 1, j == nseg - 1 ? 0 : 1, lng ? 1 : 0};
     if ((e = launch_bwd(b, stream)) != hipSuccess) return e;
     dH_in = dH_out;
   }

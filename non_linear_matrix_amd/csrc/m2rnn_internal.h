@@ -71,9 +71,15 @@ struct BwdLaunch {
   int ld;             // steps between consecutive units' rows of k, v, q, f, dy, dk, dv, dq, df (0: T)
   int dvdf_zeroed;    // 1: dv and df already hold zeros (the launcher does not clear them)
   int dW_accumulate;  // 1: dW += this call's sum (else dW =)
+  int long_kernel;    // 1: the latency-oriented reverse kernel (V in {64, 128})
 };
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream);
+// dA slots, dW partials, then the latency-oriented kernel's dv / df partials
 long long bwd_workspace_bytes(int B, int H, int T, int K, int V);
+long long bwd_long_partial_bytes(int B, int H, int T, int K, int V);
+// the latency-oriented reverse kernel and the sums of its dv / df partials (the
+// dW kernels are launch_bwd's)
+hipError_t launch_bwd_long(const BwdLaunch& p, char* dA_out, float* partials, hipStream_t stream);
 
 // Training with recomputation over segments of S steps (m2rnn_ckpt.cpp).
 long long ckpt_bytes(int B, int H, int T, int K, int V, int S);

@@ -87,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.m2rnn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, vp,
                               i, i, i, i, i, i, vp]
     lib.m2rnn_bwd.restype = i
+    lib.m2rnn_bwd_algo.argtypes = lib.m2rnn_bwd.argtypes[:-1] + [i, vp]
+    lib.m2rnn_bwd_algo.restype = i
     lib.m2rnn_frontend.argtypes = [vp, vp, fp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.m2rnn_frontend.restype = i
     lib.m2rnn_ckpt_bytes.argtypes = [i, i, i, i, i, i]
@@ -261,9 +263,10 @@ def _check_dy(dy, dH_T, B, H, T, K, V):
 
 
 def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, out=None, workspace=None,
-        stream=None) -> dict:
-    """Backward pass (m2rnn_bwd): gradients dk, dv, dq, df, dW, dH0 (fp32). `out`
-    (a dict as returned) and `workspace` may be passed to reuse buffers."""
+        stream=None, algo: str = "auto") -> dict:
+    """Backward pass (m2rnn_bwd_algo): gradients dk, dv, dq, df, dW, dH0 (fp32).
+    `out` (a dict as returned) and `workspace` may be passed to reuse buffers;
+    algo picks the reverse kernel family (any forward's `saved` is accepted)."""
     import torch
 
     lib = load()
@@ -280,11 +283,12 @@ def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, out=N
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     ptr = lambda t: None if t is None else t.data_ptr()
-    st = lib.m2rnn_bwd(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(saved), ptr(dy), ptr(dH_T),
-                       ptr(out["dk"]), ptr(out["dv"]), ptr(out["dq"]), ptr(out["df"]), ptr(out["dW"]),
-                       ptr(out["dH0"]), ptr(ws), B, H, T, K, V, DTYPES["bf16"], stream.cuda_stream)
+    st = lib.m2rnn_bwd_algo(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(saved), ptr(dy), ptr(dH_T),
+                            ptr(out["dk"]), ptr(out["dv"]), ptr(out["dq"]), ptr(out["df"]), ptr(out["dW"]),
+                            ptr(out["dH0"]), ptr(ws), B, H, T, K, V, DTYPES["bf16"], ALGOS[algo],
+                            stream.cuda_stream)
     if st != 0:
-        raise M2RNNError(st, "m2rnn_bwd")
+        raise M2RNNError(st, "m2rnn_bwd_algo")
     out["workspace"] = ws  # keep alive until the stream has run
     return out
 

@@ -231,6 +231,14 @@ def test_training_forwards_take_the_long_kernel_only_where_the_backward_covers_t
                                                2, 2, 64, K, 64, 16, bf16, a, None)
         assert rc(16) == UNSUPPORTED, algo
         assert lib.m2rnn_fwd_save(None, p, p, p, p, None, p, None, p, 2, 2, 16, 64, 64, bf16, a, None) == INVALID
+        bw = lambda K, V, alg=a, dk=p: lib.m2rnn_bwd_algo(p, p, p, p, p, None, p, p, None, dk, p, p, p, p, None, p,
+                                                          2, 2, 16, K, V, bf16, alg, None)
+        assert bw(16, 64) == UNSUPPORTED, algo
+        assert bw(64, 64, dk=None) == INVALID, algo
+    for other in ("simple", 6, 99):
+        alg = m2rnn.ALGOS[other] if isinstance(other, str) else other
+        assert lib.m2rnn_bwd_algo(p, p, p, p, p, None, p, p, None, p, p, p, p, p, None, p, 2, 2, 16, 64, 64, bf16,
+                                  alg, None) == UNSUPPORTED, other
 
 
 def test_frontend_validates_before_launching():

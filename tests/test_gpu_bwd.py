@@ -38,7 +38,7 @@ def _grads(cfg, seed, algo="auto", with_dHT=True):
     d = to_device(x)
     y, HT, saved = m2rnn.fwd_save(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], algo=algo)
     g = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, torch.from_numpy(dy).cuda(),
-                  None if dHT is None else torch.from_numpy(dHT).cuda())
+                  None if dHT is None else torch.from_numpy(dHT).cuda(), algo=algo)
     torch.cuda.synchronize()
     got = {key: g[key].cpu().numpy() for key in GRADS}
     got["y"], got["H_T"] = y.cpu().numpy(), HT.cpu().numpy()
@@ -58,7 +58,8 @@ SHAPES = [
 ]
 
 
-# "auto" takes the latency-oriented saving forward on these few-tile shapes (T > 1)
+# "auto" takes the latency-oriented forward and reverse kernels on these few-tile
+# shapes (T > 1); "mfma_split" the one-wave-per-tile ones
 @pytest.mark.parametrize("algo", ["auto", "mfma_split"])
 @pytest.mark.parametrize("name,shape", SHAPES)
 def test_gradients_match_the_oracle(name, shape, algo):
@@ -104,6 +105,30 @@ def test_single_operand_forward_feeds_the_same_backward():
     got, ref = _grads(cfg, 33, algo="mfma")
     for key in GRADS:
         assert nerr(got[key], ref[key]) <= TOL, key
+
+
+def test_the_two_reverse_kernels_agree():
+    """Both reverse-time kernels on one saved buffer: the same per-element
+    arithmetic, sums in other orders (dq and dk over column blocks, dv and df
+    over row tiles, dA W^T over blocks), so the gradients agree to fp32
+    summation order, amplified along the sequence."""
+    import torch
+    from non_linear_matrix_amd import m2rnn
+
+    for cfg in (scaled(CONFIGS["C3"], B=2, H=2, T=40), scaled(CONFIGS["C2"], B=2, H=3, T=33, K=32)):
+        announce(f"reverse kernels agree K={cfg.K} V={cfg.V} T={cfg.T}")
+        x = generate(cfg, 36)
+        d = to_device(x)
+        dy = torch.randn((cfg.B, cfg.H, cfg.T, cfg.V), generator=torch.Generator().manual_seed(9)).cuda()
+        dHT = torch.randn((cfg.B, cfg.H, cfg.K, cfg.V), generator=torch.Generator().manual_seed(10)).cuda()
+        _, _, saved = m2rnn.fwd_save(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], algo="mfma_split")
+        g1 = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, dy, dHT, algo="mfma_split")
+        g2 = m2rnn.bwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], saved, dy, dHT, algo="mfma_long_split")
+        torch.cuda.synchronize()
+        for key in GRADS:
+            a, b = g1[key].cpu().numpy(), g2[key].cpu().numpy()
+            assert np.all(np.isfinite(b)), key
+            assert nerr(b, a.astype(np.float64)) <= 1e-3, (key, nerr(b, a.astype(np.float64)))
 
 
 def test_backward_is_deterministic():
