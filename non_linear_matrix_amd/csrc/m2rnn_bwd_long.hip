@@ -113,6 +113,7 @@ struct BwdLongArgs {
   char* dA_out;    // per-step bf16 dA in the saved layout (read by the dW kernel)
   float* dv_part;  // [K/16][B H][T][V]: each row tile's dv_t
   float* df_part;  // [K/16][B H][T]: each row tile's df_t
+  char* dA_sink;   // one saved-layout slot that takes the inert steps' dA stores
   int B, H, T, K;
   long long ld;    // row stride (in steps) of the per-step inputs and of dk, dq
 };
@@ -245,18 +246,19 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
   if (nchunks > 1) st.load(a, unit, row0, 1);
 
   // saved data of step index i (t = T - 1 - i): the state operand c H_t (slot
-  // t + 1, H0 for t = -1) and the pre-activation c A_t, this lane's 16 bytes
+  // t + 1, H0 for t = -1) and the pre-activation c A_t, this lane's 16 bytes.
+  // Inert steps (t < 0) read a clamped step: any finite data does, since their
+  // gate 1 zeroes dA and their dy, v, q are zero. The loads carry no branch, so
+  // the waits for them count exactly the operations issued after them.
   auto load_state = [&](long long i) {
     const long long t = (long long)T - 1 - i;
-    return t >= -1 ? *reinterpret_cast<const u4*>(a.saved + saved_state_off(unit, static_cast<int>(t + 1), T, K, V) +
-                                                  lane_off)
-                   : u4{0, 0, 0, 0};
+    const int slot = static_cast<int>(t + 1 < 0 ? 0 : t + 1);
+    return *reinterpret_cast<const u4*>(a.saved + saved_state_off(unit, slot, T, K, V) + lane_off);
   };
   auto load_pre = [&](long long i) {
     const long long t = (long long)T - 1 - i;
-    return t >= 0 ? *reinterpret_cast<const u4*>(a.saved + saved_pre_off(unit, static_cast<int>(t), a.B, a.H, T, K, V) +
-                                                 lane_off)
-                  : u4{0, 0, 0, 0};
+    const int tc = static_cast<int>(t < 0 ? 0 : t);
+    return *reinterpret_cast<const u4*>(a.saved + saved_pre_off(unit, tc, a.B, a.H, T, K, V) + lane_off);
   };
   // rings indexed by step index mod kRing: state i is read at steps i and i - 1,
   // the pre-activation at step i
@@ -284,6 +286,42 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
     const float2* fss = reinterpret_cast<const float2*>(lds + L::FS_OFF) + buf * kChunk;
     const int t_first = T - 1 - kChunk * c;
 
+    // Per step: the parts that need the incoming dA_{t+1} W^T (the critical
+    // path to the next exchange) come first; everything that depends only on
+    // staged inputs and saved data (r, r (1 - r), q_t dy_t, the dq partial) is
+    // formed one step early, while the previous step waits for its products; the
+    // dk and df partials and the dA store follow the products' issue.
+    struct Pre {
+      float r[8], rr[8], qdy[8];
+      float dqp;
+    };
+    auto precompute = [&](int sj) {  // step sj of this chunk
+      Pre x;
+      const u4 sc = sring[sj % kRing], uu = pring[sj % kRing];
+      const float qn = qks[sj * 16 + n].x;
+      float dqp = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int cc = 2 * w + j;
+        const float4 d01 = *reinterpret_cast<const float4*>(dvs + sj * V + 16 * cc + 4 * g);
+        const float4 d23 = *reinterpret_cast<const float4*>(dvs + sj * V + 16 * cc + 4 * g + 2);
+        const float dyv[4] = {d01.x, d01.z, d23.x, d23.z};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int jj = 4 * j + e;
+          const float hcur = (jj & 1) ? hi_bf16(sc[jj / 2]) : lo_bf16(sc[jj / 2]);  // c H_t
+          const float u = (jj & 1) ? hi_bf16(uu[jj / 2]) : lo_bf16(uu[jj / 2]);     // c A_t
+          const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
+          x.r[jj] = r;
+          x.rr[jj] = fmaf(-r, r, r);
+          x.qdy[jj] = qn * dyv[e];
+          dqp = fmaf(hcur, dyv[e], dqp);
+        }
+      }
+      x.dqp = dqp;
+      return x;
+    };
+    Pre pre;
     static_for<kChunk>([&](auto si) {
       constexpr int s = decltype(si)::value;
       const long long i = (long long)kChunk * c + s;  // step index
@@ -291,54 +329,26 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
       // saved data kAhead steps on
       sring[(s + kAhead + 1) % kRing] = load_state(i + kAhead + 1);
       pring[(s + kAhead) % kRing] = load_pre(i + kAhead);
-      const u4 sc = sring[s % kRing], sp = sring[(s + 1) % kRing], uu = pring[s % kRing];
+      if constexpr (s == 0) pre = precompute(0);  // the chunk was staged only now
       const float2 fa = fss[s];
       const float fg = fa.x, a4 = fa.y;
-      const float2 qk = qks[s * 16 + n];
-      float dqp = 0.0f, dkp = 0.0f, dfp = 0.0f;
-      f4 dA[2];
+      // critical: G and dA of this wave's 8 elements, then the exchange
+      f4 gvv[2], dA[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int cc = 2 * w + j;
-        const float4 d01 = *reinterpret_cast<const float4*>(dvs + s * V + 16 * cc + 4 * g);
-        const float4 d23 = *reinterpret_cast<const float4*>(dvs + s * V + 16 * cc + 4 * g + 2);
-        const float dyv[4] = {d01.x, d01.z, d23.x, d23.z};
-        const float vv[4] = {d01.y, d01.w, d23.y, d23.w};
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int jj = 4 * j + e;  // element of this wave's block
-          const float hcur = (jj & 1) ? hi_bf16(sc[jj / 2]) : lo_bf16(sc[jj / 2]);  // c H_t
-          const float hprv = (jj & 1) ? hi_bf16(sp[jj / 2]) : lo_bf16(sp[jj / 2]);  // c H_{t-1}
-          const float u = (jj & 1) ? hi_bf16(uu[jj / 2]) : lo_bf16(uu[jj / 2]);     // c A_t
-          float gv = fmaf(fnext, G[j][e], cur[j][e]);
-          gv = fmaf(qk.x, dyv[e], gv);
-          dqp = fmaf(hcur, dyv[e], dqp);
-          const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
-          const float d = (a4 * gv) * fmaf(-r, r, r);
-          dfp = fmaf(fmaf(2.0f, r, fmaf(hprv, kInvC, -1.0f)), gv, dfp);
-          dkp = fmaf(d, vv[e], dkp);
+          const int jj = 4 * j + e;
+          const float gv = fmaf(fnext, G[j][e], cur[j][e]) + pre.qdy[jj];
           G[j][e] = gv;
-          dA[j][e] = d;
+          gvv[j][e] = gv;
+          dA[j][e] = (a4 * gv) * pre.rr[jj];
         }
-      }
       const u4 pk = u4{pack_bf16(dA[0][0], dA[0][1]), pack_bf16(dA[0][2], dA[0][3]),
                        pack_bf16(dA[1][0], dA[1][1]), pack_bf16(dA[1][2], dA[1][3])};
       const bf16x8 Bown = __builtin_bit_cast(bf16x8, pk);
       // this wave's dA block into the shared tile (row n, columns 32 w + 8 g ..)
       *reinterpret_cast<u4*>(hb + (s & (NHS - 1)) * 16 * HROW + n * HROW + 32 * w + 8 * g) = pk;
-      if (t >= 0) *reinterpret_cast<u4*>(a.dA_out + (unit * T + t) * saved_slot_bytes(K, V) + lane_off) = pk;
-      // row partials over this wave's columns, and its df partial
-      dqp += __shfl_xor(dqp, 16);
-      dqp += __shfl_xor(dqp, 32);
-      dkp += __shfl_xor(dkp, 16);
-      dkp += __shfl_xor(dkp, 32);
-      if (g == 0) {
-        rs[(w * kChunk + s) * 16 + n] = dqp;
-        rs[((S + w) * kChunk + s) * 16 + n] = dkp;
-      }
-#pragma unroll
-      for (int m = 1; m < 64; m *= 2) dfp += __shfl_xor(dfp, m);
-      if (l == 0) dfs[w * kChunk + s] = dfp;
       // dA_t W^T on this wave's two output tiles: own block first
       f4 acc[2];
 #pragma unroll
@@ -355,6 +365,39 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
       for (int o = 1; o < KB; ++o)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[j] = mfma(Wp[j][o], Bo[o], acc[j]);
+      // off the critical path: dk, df and dq partials, the dA store
+      {
+        const u4 sp = sring[(s + 1) % kRing];
+        float dkp = 0.0f, dfp = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int cc = 2 * w + j;
+          const float4 d01 = *reinterpret_cast<const float4*>(dvs + s * V + 16 * cc + 4 * g);
+          const float4 d23 = *reinterpret_cast<const float4*>(dvs + s * V + 16 * cc + 4 * g + 2);
+          const float vv[4] = {d01.y, d01.w, d23.y, d23.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jj = 4 * j + e;
+            const float hprv = (jj & 1) ? hi_bf16(sp[jj / 2]) : lo_bf16(sp[jj / 2]);  // c H_{t-1}
+            dfp = fmaf(fmaf(2.0f, pre.r[jj], fmaf(hprv, kInvC, -1.0f)), gvv[j][e], dfp);
+            dkp = fmaf(dA[j][e], vv[e], dkp);
+          }
+        }
+        float dqp = pre.dqp;
+        dqp += __shfl_xor(dqp, 16);
+        dqp += __shfl_xor(dqp, 32);
+        dkp += __shfl_xor(dkp, 16);
+        dkp += __shfl_xor(dkp, 32);
+#pragma unroll
+        for (int m = 1; m < 64; m *= 2) dfp += __shfl_xor(dfp, m);
+        // every lane of a row (or of the wave) holds the same sum: no branch
+        rs[(w * kChunk + s) * 16 + n] = dqp;
+        rs[((S + w) * kChunk + s) * 16 + n] = dkp;
+        dfs[w * kChunk + s] = dfp;
+        char* dst = t >= 0 ? a.dA_out + (unit * T + t) * saved_slot_bytes(K, V) : a.dA_sink;
+        *reinterpret_cast<u4*>(dst + lane_off) = pk;
+      }
+      if constexpr (s + 1 < kChunk) pre = precompute(s + 1);
       // dv: read out the step pair (s - 1, s) on this wave's columns
       if constexpr ((s & 1) != 0) {
         const int p = g / 2, rr = 8 * (g % 2), sq = s - 1 + p;
@@ -457,7 +500,7 @@ __global__ void bwd_long_sums_kernel(const float* dv_part, const float* df_part,
 }  // namespace
 
 long long bwd_long_partial_bytes(int B, int H, int T, int K, int V) {
-  return (long long)(K / 16) * B * H * T * (V + 1) * 4;
+  return (long long)(K / 16) * B * H * T * (V + 1) * 4 + 16 + saved_slot_bytes(K, V);
 }
 
 hipError_t launch_bwd_long(const BwdLaunch& p, char* dA_out, float* partials, hipStream_t stream) {
@@ -469,7 +512,10 @@ hipError_t launch_bwd_long(const BwdLaunch& p, char* dA_out, float* partials, hi
                 static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.f),
                 static_cast<const unsigned short*>(p.W), static_cast<const char*>(p.saved), p.dy, p.dHT,
                 p.dk, p.dq, p.dH0, dA_out, partials, partials + (long long)(p.K / 16) * BH * p.T * p.V,
-                p.B, p.H, p.T, p.K, p.ld > 0 ? (long long)p.ld : (long long)p.T};
+                nullptr, p.B, p.H, p.T, p.K, p.ld > 0 ? (long long)p.ld : (long long)p.T};
+  // the sink slot after the df partials, 16-byte aligned
+  const long long sink_off = ((long long)(p.K / 16) * BH * p.T * (p.V + 1) * 4 + 15) / 16 * 16;
+  a.dA_sink = reinterpret_cast<char*>(partials) + sink_off;
   if (p.V == 128)
     hipLaunchKernelGGL((mfma_bwd_long_kernel<128>), dim3((unsigned)grid), dim3(BwdLongLayout<128>::THREADS), 0,
                        stream, a);
