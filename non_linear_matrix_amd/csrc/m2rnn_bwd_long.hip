@@ -59,6 +59,14 @@ __device__ __forceinline__ unsigned int pack_bf16(float x0, float x1) {
 __device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// sum over the 16 lanes of a DPP row; every lane of the row ends with the total
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // mirror
+  return x;
+}
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -85,8 +93,8 @@ struct BwdLongLayout {
   static constexpr int KS_BYTES = 2 * kChunk * 16 * 2;  // k as bf16 (readout B operand)
   static constexpr int FS_BYTES = 2 * kChunk * 8;       // (f, 4 (1 - f)) per step
   static constexpr int HB_BYTES = NHS * 16 * HROW * 2;
-  static constexpr int RS_BYTES = 2 * S * kChunk * 16 * 4;  // dq, dk partials per (wave, step, row)
-  static constexpr int DF_BYTES = S * kChunk * 4;           // df partials per (wave, step)
+  static constexpr int RS_BYTES = 2 * S * kChunk * 64 * 4;  // dq, dk partials per (wave, step, lane)
+  static constexpr int DF_BYTES = S * kChunk * 64 * 4;      // df partials per (wave, step, lane)
   static constexpr int DV_OFF = 0;
   static constexpr int QK_OFF = DV_OFF + DV_BYTES;
   static constexpr int KS_OFF = QK_OFF + QK_BYTES;
@@ -207,8 +215,8 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
   const int nchunks = (T + kChunk - 1) / kChunk;
 
   unsigned short* hb = reinterpret_cast<unsigned short*>(lds + L::HB_OFF);
-  float* rs = reinterpret_cast<float*>(lds + L::RS_OFF);  // [2][S][kChunk][16]
-  float* dfs = reinterpret_cast<float*>(lds + L::DF_OFF);  // [S][kChunk]
+  float* rs = reinterpret_cast<float*>(lds + L::RS_OFF);  // [2][S][kChunk][64 lanes]
+  float* dfs = reinterpret_cast<float*>(lds + L::DF_OFF);  // [S][kChunk][64 lanes]
 
   // W fragments of this wave's output tiles cc = 2w + j against every block
   // b = (w + o) mod KB (rotated so that register indices are compile-time):
@@ -383,17 +391,11 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
             dkp = fmaf(dA[j][e], vv[e], dkp);
           }
         }
-        float dqp = pre.dqp;
-        dqp += __shfl_xor(dqp, 16);
-        dqp += __shfl_xor(dqp, 32);
-        dkp += __shfl_xor(dkp, 16);
-        dkp += __shfl_xor(dkp, 32);
-#pragma unroll
-        for (int m = 1; m < 64; m *= 2) dfp += __shfl_xor(dfp, m);
-        // every lane of a row (or of the wave) holds the same sum: no branch
-        rs[(w * kChunk + s) * 16 + n] = dqp;
-        rs[((S + w) * kChunk + s) * 16 + n] = dkp;
-        dfs[w * kChunk + s] = dfp;
+        // each lane's partials to its own word (no branch, no two lanes on one
+        // address); df first summed over the 16 lanes of each row
+        rs[(w * kChunk + s) * 64 + l] = pre.dqp;
+        rs[((S + w) * kChunk + s) * 64 + l] = dkp;
+        dfs[(w * kChunk + s) * 64 + l] = row_sum16(dfp);
         char* dst = t >= 0 ? a.dA_out + (unit * T + t) * saved_slot_bytes(K, V) : a.dA_sink;
         *reinterpret_cast<u4*>(dst + lane_off) = pk;
       }
@@ -433,24 +435,30 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
       Dr[0] = f4{0, 0, 0, 0};
       Dr[1] = f4{0, 0, 0, 0};
     }
-    // dq, dk: the waves' partials of each (step, row), in wave order (visible
-    // since the last step's barrier)
+    // the last step wrote its partials after its barrier
+    lds_barrier();
+    // dq, dk: the partials of each (step, row) over the waves and the four lane
+    // groups, in a fixed order
     for (int idx = tid; idx < kChunk * 16; idx += L::THREADS) {
       const int s = idx / 16, row = idx % 16, t = t_first - s;
       if (t < 0) continue;
       float q = 0.0f, kk = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < S; ++ww) {
-        q += rs[(ww * kChunk + s) * 16 + row];
-        kk += rs[((S + ww) * kChunk + s) * 16 + row];
-      }
+      for (int ww = 0; ww < S; ++ww)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          q += rs[(ww * kChunk + s) * 64 + 16 * gg + row];
+          kk += rs[((S + ww) * kChunk + s) * 64 + 16 * gg + row];
+        }
       a.dq[(unit * a.ld + t) * K + row0 + row] = q * kInvC;
       a.dk[(unit * a.ld + t) * K + row0 + row] = kk;
     }
-    if (tid < kChunk && t_first - tid >= 0) {
+    if (tid < kChunk && t_first - tid >= 0) {  // df: the row totals of every wave
       float sum = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < S; ++ww) sum += dfs[ww * kChunk + tid];
+      for (int ww = 0; ww < S; ++ww)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) sum += dfs[(ww * kChunk + tid) * 64 + 16 * gg];
       a.df_part[(rt * BH + unit) * T + (t_first - tid)] = sum;
     }
     // next chunk's inputs; the barrier also orders these reads before the next
