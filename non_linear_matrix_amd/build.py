@@ -1,4 +1,5 @@
-"""Build the HIP library libm2rnn.so in-tree for gfx950 (hipcc, no GPU needed).
+"""Build the HIP library libm2rnn.so in-tree for gfx950 (hipcc, no GPU needed),
+and the issue-rate probe program beside it.
 
     python -m non_linear_matrix_amd.build
 """
@@ -14,6 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libm2rnn.so")
+PROBE = os.path.join(PKG, "issue_probe")
 SOURCES = ["m2rnn_api.cpp", "m2rnn_simple.hip", "m2rnn_mfma.hip", "m2rnn_bwd.hip", "m2rnn_ckpt.cpp", "m2rnn_frontend.hip", "m2rnn_decode.hip", "m2rnn_long.hip", "m2rnn_bwd_long.hip"]
 ARCH = "gfx950"
 
@@ -25,18 +27,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17",
             # packed fp32 VALU forms are kept out of the device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # MFMA results land in arch VGPRs, where the fused epilogue reads them
-            "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-I", INCLUDE, "-I", CSRC] + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out]
+            "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def run(cmd: list, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,6 +45,25 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg, file=sys.stderr)
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The issue-rate probe (csrc/issue_probe.hip), a standalone program."""
+    tmp = PROBE + ".tmp"
+    run([hipcc()] + flags() + [os.path.join(CSRC, "issue_probe.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PROBE)
+    return PROBE
+
+
+def command(out: str) -> list:
+    return ([hipcc()] + flags() + ["-fPIC", "-shared", "-I", INCLUDE, "-I", CSRC]
+            + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out])
+
+
+def build(verbose: bool = False) -> str:
+    build_probe(verbose)
+    tmp = LIB + ".tmp"
+    run(command(tmp), verbose)
     os.replace(tmp, LIB)
     return LIB
 
