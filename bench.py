@@ -43,8 +43,8 @@ TRAFFIC_KIB = {
                      "1bc0c826cba1f59652c2940f5936aa56c2d4934b27d12aea700f6c8b1cf29904"),
     ("D1", "mfma"): (267823.2, 530624.2, "m2rnn_decode.hip",
                      "956ca12e91e2af7f990630af4aead6a5a4ebb04ffc1229b7d6494d0c06ac9e4f"),
-    ("C5", "mfma_long_split"): (1053877.5, 2098176.0, "m2rnn_long.hip",
-                                "4c52129bce177f227f979525e531b2529635ed96cb57b2b111d6a1b2d98a5e4d"),
+    ("C5", "mfma_long_split"): (1053878.0, 2098176.0, "m2rnn_long.hip",
+                                "ce6094f04770b50e1f8726b4551d9001eb9c393746370b8de05fb13789e5c6bd"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the

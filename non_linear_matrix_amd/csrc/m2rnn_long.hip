@@ -447,8 +447,16 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
       ReadoutOps ro;
       if constexpr ((s & 1) != 0) ro = readout_load(sb, s - 1, 2);
       fetch_others(s & (NHS - 1), s & 1);
+      // tile by tile: tile 0's sum is complete while tile 1's last KB - 1
+      // blocks (twice as many MFMAs when split) still run, and the next step's
+      // epilogue of tile 0 issues under them
 #pragma unroll
-      for (int o = 1; o < KB; ++o) products(o, accn);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int o = 1; o < KB; ++o) {
+          accn[j] = mfma(Wf[j][o], Bf[o], accn[j]);
+          if constexpr (SPLIT) accn[j] = mfma(Wf[j][o], Bl[o], accn[j]);
+        }
       acc[0] = accn[0];
       acc[1] = accn[1];
       if constexpr ((s & 1) != 0) readout_mma(ro);
