@@ -102,6 +102,11 @@ struct BwdArgs {
   const float *dy, *dHT;
   float *dk, *dv, *dq, *df, *dH0;
   char* dA_out;  // per-step bf16 dA, one saved-layout slot per (unit, t) (read by the dW kernel)
+  // stores that must not land (a padding step's dA, the dq and dk of lanes that
+  // do not own a row) go here, so that no store sits behind a branch: a global
+  // memory wait could then count them only conservatively, and would drain the
+  // stores issued since the saved-data prefetch at every step
+  char* sink;
   int B, H, T, K;
   long long ld;  // row stride (in steps) of the per-step inputs and gradients
 };
@@ -242,15 +247,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_bwd_kernel(BwdArgs a) {
     for (int b = 0; b < KB; ++b) r.x[b] = *reinterpret_cast<const u4*>(a.saved + off + lane_off + b * 1024);
     return r;
   };
-  auto zero_slot = [&]() {
-    Saved r;
-#pragma unroll
-    for (int b = 0; b < KB; ++b) r.x[b] = u4{0, 0, 0, 0};
-    return r;
-  };
-  // state operand c H_t of step t (slot t + 1; t = -1 is H0), pre-activation c A_t
-  auto state_of = [&](int t) { return t >= -1 ? load_slot(saved_state_off(unit, t + 1, T, K, V)) : zero_slot(); };
-  auto pre_of = [&](int t) { return t >= 0 ? load_slot(saved_pre_off(unit, t, a.B, a.H, T, K, V)) : zero_slot(); };
+  // state operand c H_t of step t (slot t + 1; t = -1 is H0), pre-activation c A_t.
+  // Padding steps (t < 0) read the nearest real slot instead, without a branch:
+  // their gate is 1 and their dy 0, so their dA is exactly 0 for any finite data.
+  auto state_of = [&](int t) { return load_slot(saved_state_off(unit, max(t, -1) + 1, T, K, V)); };
+  auto pre_of = [&](int t) { return load_slot(saved_pre_off(unit, max(t, 0), a.B, a.H, T, K, V)); };
 
   Saved s_cur = state_of(T - 1), s_prev = state_of(T - 2), u_cur = pre_of(T - 1);
 
@@ -365,7 +366,10 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_bwd_kernel(BwdArgs a) {
                          pack_bf16(dA[1][0], dA[1][1]), pack_bf16(dA[1][2], dA[1][3])};
         const bf16x8 Bd = __builtin_bit_cast(bf16x8, pk);
         *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bd;
-        if (t >= 0) *reinterpret_cast<u4*>(a.dA_out + (unit * T + t) * saved_slot_bytes(K, V) + lane_off + b * 1024) = pk;
+        {
+          char* dst = t >= 0 ? a.dA_out + (unit * T + t) * saved_slot_bytes(K, V) : a.sink;
+          *reinterpret_cast<u4*>(dst + lane_off + b * 1024) = pk;
+        }
 #pragma unroll
         for (int cc = 0; cc < CT; ++cc) acc[cc] = mfma(Wp[cc][b], Bd, acc[cc]);
       }
@@ -374,9 +378,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_bwd_kernel(BwdArgs a) {
       dqp += __shfl_xor(dqp, 32);
       dkp += __shfl_xor(dkp, 16);
       dkp += __shfl_xor(dkp, 32);
-      if (g == 0 && t >= 0) {
-        a.dq[(unit * a.ld + t) * K + my_row] = dqp * kInvC;
-        a.dk[(unit * a.ld + t) * K + my_row] = dkp;
+      {
+        const bool own = g == 0 && t >= 0;
+        float* sinkf = reinterpret_cast<float*>(a.sink + saved_slot_bytes(K, V));
+        *(own ? a.dq + (unit * a.ld + t) * K + my_row : sinkf + l) = dqp * kInvC;
+        *(own ? a.dk + (unit * a.ld + t) * K + my_row : sinkf + 64 + l) = dkp;
       }
       // df over the tile
 #pragma unroll
@@ -555,16 +561,21 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* partial, float* dW, bool zeroed
 
 }  // namespace
 
+// workspace: the dA slots, the dW partials, the long reverse kernel's partials,
+// then the multi-step reverse kernel's sink (one slot and 128 floats)
 long long bwd_workspace_bytes(int B, int H, int T, int K, int V) {
   return (long long)B * H * T * saved_slot_bytes(K, V) + (long long)H * dw_splits(B, T, K) * V * V * 4 +
-         ((V == 64 || V == 128) ? bwd_long_partial_bytes(B, H, T, K, V) : 0);
+         ((V == 64 || V == 128) ? bwd_long_partial_bytes(B, H, T, K, V) : 0) + saved_slot_bytes(K, V) + 512;
 }
 
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream) {
   BwdArgs a{static_cast<const unsigned short*>(p.k), static_cast<const unsigned short*>(p.v),
             static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.f),
             static_cast<const unsigned short*>(p.W), static_cast<const char*>(p.saved), p.dy, p.dHT,
-            p.dk, p.dv, p.dq, p.df, p.dH0, static_cast<char*>(p.workspace), p.B, p.H, p.T, p.K,
+            p.dk, p.dv, p.dq, p.df, p.dH0, static_cast<char*>(p.workspace),
+            static_cast<char*>(p.workspace) + bwd_workspace_bytes(p.B, p.H, p.T, p.K, p.V) -
+                (saved_slot_bytes(p.K, p.V) + 512),
+            p.B, p.H, p.T, p.K,
             p.ld > 0 ? (long long)p.ld : (long long)p.T};
   const bool z = p.dvdf_zeroed != 0, acc = p.dW_accumulate != 0;
   float* partial = reinterpret_cast<float*>(static_cast<char*>(p.workspace) +
