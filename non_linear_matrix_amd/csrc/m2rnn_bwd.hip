@@ -561,11 +561,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* partial, float* dW, bool zeroed
 
 }  // namespace
 
+// the multi-step reverse kernel's sink: one dA slot, then 128 floats for dq and dk
+static long long bwd_sink_bytes(int K, int V) { return saved_slot_bytes(K, V) + 512; }
+
 // workspace: the dA slots, the dW partials, the long reverse kernel's partials,
-// then the multi-step reverse kernel's sink (one slot and 128 floats)
+// then the sink
 long long bwd_workspace_bytes(int B, int H, int T, int K, int V) {
   return (long long)B * H * T * saved_slot_bytes(K, V) + (long long)H * dw_splits(B, T, K) * V * V * 4 +
-         ((V == 64 || V == 128) ? bwd_long_partial_bytes(B, H, T, K, V) : 0) + saved_slot_bytes(K, V) + 512;
+         ((V == 64 || V == 128) ? bwd_long_partial_bytes(B, H, T, K, V) : 0) + bwd_sink_bytes(K, V);
 }
 
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream) {
@@ -573,8 +576,7 @@ hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream) {
             static_cast<const unsigned short*>(p.q), static_cast<const unsigned short*>(p.f),
             static_cast<const unsigned short*>(p.W), static_cast<const char*>(p.saved), p.dy, p.dHT,
             p.dk, p.dv, p.dq, p.df, p.dH0, static_cast<char*>(p.workspace),
-            static_cast<char*>(p.workspace) + bwd_workspace_bytes(p.B, p.H, p.T, p.K, p.V) -
-                (saved_slot_bytes(p.K, p.V) + 512),
+            static_cast<char*>(p.workspace) + bwd_workspace_bytes(p.B, p.H, p.T, p.K, p.V) - bwd_sink_bytes(p.K, p.V),
             p.B, p.H, p.T, p.K,
             p.ld > 0 ? (long long)p.ld : (long long)p.T};
   const bool z = p.dvdf_zeroed != 0, acc = p.dW_accumulate != 0;
