@@ -117,9 +117,16 @@ enum {
    * The library then never clears y itself, so a caller that zeroes y first
    * gets the plain result with the recurrence as the only kernel on the stream. */
   M2RNN_FLAG_ACCUMULATE_Y = 1u,
-  /* Every output bitwise repeatable from run to run: AUTO then keeps to the
-   * kernels whose y has a fixed summation order, and MFMA_LONG* with T > 1
-   * (whose y adds over row tiles are atomic) is NOT_SUPPORTED. */
+  /* Every output bitwise repeatable from run to run. H_T always is; y is
+   * whenever each element receives at most one atomic contribution, or two onto
+   * a y the call cleared itself. The families that add partial readouts into y
+   * atomically are MFMA and MFMA_SPLIT at K = 128 (two workgroups per unit) and
+   * MFMA_LONG* with T > 1 (K/16 row tiles per unit; T = 1 on the matrix-core
+   * shapes runs the decoding kernel, which has no atomics). Under this flag AUTO
+   * keeps to a combination that is repeatable (MFMA_SPLIT in place of
+   * MFMA_LONG_SPLIT, SIMPLE where nothing else is), and an explicit family that
+   * is not (three or more adds per element, or two together with
+   * M2RNN_FLAG_ACCUMULATE_Y) is NOT_SUPPORTED. */
   M2RNN_FLAG_DETERMINISTIC = 2u
 };
 
@@ -297,6 +304,14 @@ typedef struct m2rnn_plan {
  * sizes < 1; NOT_SUPPORTED as m2rnn_check_args. */
 m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                             m2rnn_algo algo, m2rnn_plan* plan);
+
+/* m2rnn_get_plan for a call of m2rnn_fwd_ex / m2rnn_fwd_varlen with `flags`:
+ * plan->algo is the family that call runs (AUTO resolved under the flags'
+ * rules), and the status is the one that call would return before launching
+ * (NOT_SUPPORTED for unknown flag bits or a deterministic call on a family that
+ * sums y atomically). Host only. */
+m2rnn_status m2rnn_get_plan_ex(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                               m2rnn_algo algo, unsigned flags, m2rnn_plan* plan);
 
 /* Static text for a status code ("unknown status" for other values). */
 const char* m2rnn_status_string(m2rnn_status status);

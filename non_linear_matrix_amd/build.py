@@ -1,7 +1,9 @@
-"""Build the HIP library libm2rnn.so in-tree for gfx950 (hipcc, no GPU needed),
-and the issue-rate probe program beside it.
+"""Build the HIP library libm2rnn.so in-tree for gfx950 (hipcc, no GPU needed).
 
     python -m non_linear_matrix_amd.build
+
+Each source compiles to its own object in `_build/` (in parallel), then one
+link makes the shared library.
 """
 from __future__ import annotations
 
@@ -9,14 +11,16 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libm2rnn.so")
-PROBE = os.path.join(PKG, "issue_probe")
-SOURCES = ["m2rnn_api.cpp", "m2rnn_simple.hip", "m2rnn_mfma.hip", "m2rnn_bwd.hip", "m2rnn_ckpt.cpp", "m2rnn_frontend.hip", "m2rnn_decode.hip", "m2rnn_long.hip", "m2rnn_bwd_long.hip"]
+OBJDIR = os.path.join(ROOT, "_build")
+SOURCES = ["m2rnn_api.cpp", "m2rnn_simple.hip", "m2rnn_mfma.hip", "m2rnn_bwd.hip", "m2rnn_ckpt.cpp",
+           "m2rnn_frontend.hip", "m2rnn_decode.hip", "m2rnn_long.hip", "m2rnn_bwd_long.hip"]
 ARCH = "gfx950"
 
 
@@ -47,23 +51,24 @@ def run(cmd: list, verbose: bool) -> None:
         print(msg, file=sys.stderr)
 
 
-def build_probe(verbose: bool = False) -> str:
-    """The issue-rate probe (csrc/issue_probe.hip), a standalone program."""
-    tmp = PROBE + ".tmp"
-    run([hipcc()] + flags() + [os.path.join(CSRC, "issue_probe.hip"), "-o", tmp], verbose)
-    os.replace(tmp, PROBE)
-    return PROBE
+def compile_command(src: str, obj: str) -> list:
+    return [hipcc()] + flags() + ["-fPIC", "-c", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, src), "-o", obj]
 
 
 def command(out: str) -> list:
+    """One-step build of the whole library (the same flags as the per-object build)."""
     return ([hipcc()] + flags() + ["-fPIC", "-shared", "-I", INCLUDE, "-I", CSRC]
             + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out])
 
 
-def build(verbose: bool = False) -> str:
-    build_probe(verbose)
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 8)
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        list(pool.map(lambda so: run(compile_command(*so), verbose), zip(SOURCES, objs)))
     tmp = LIB + ".tmp"
-    run(command(tmp), verbose)
+    run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -78,6 +78,42 @@ m2rnn_status training_algo(m2rnn_algo& algo, int B, int H, int T, int K, int V, 
 bool is_long(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT; }
 bool is_split(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_SPLIT || algo == M2RNN_ALGO_MFMA_LONG_SPLIT; }
 
+// Whether a forward call's y has one fixed summation order (bitwise repeatable).
+// Kernels whose workgroups share a unit add their readouts into y atomically:
+// the multi-step kernels' K/(16 NW) workgroups and the long kernels' K/16 row
+// tiles. One contribution per element, or two onto a cleared y (0 + a + b =
+// 0 + b + a exactly), cannot depend on the order; two onto a y that already holds
+// values (M2RNN_FLAG_ACCUMULATE_Y) or three and more can. One step on the
+// matrix-core shapes runs the decoding kernel, which sums in LDS in a fixed order.
+bool atomic_free(m2rnn_algo algo, int T, int K, int V, bool bf16, bool accumulate) {
+  int adds = 1;
+  const bool decode = T == 1 && m2rnn::mfma_supports(K, V, bf16);
+  if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT) adds = decode ? 1 : m2rnn::mfma_groups(K);
+  if (is_long(algo)) adds = decode ? 1 : K / 16;
+  return adds <= 1 || (adds == 2 && !accumulate);
+}
+
+// The kernel family a forward call runs: AUTO resolved, and the rules of the
+// flags applied (unknown flag bits and a deterministic call on a family that
+// sums y atomically are NOT_SUPPORTED). Host only.
+m2rnn_status resolve_algo(m2rnn_algo& algo, int B, int H, int T, int K, int V, m2rnn_dtype dt, unsigned flags) {
+  if ((flags & ~static_cast<unsigned>(M2RNN_FLAG_ACCUMULATE_Y | M2RNN_FLAG_DETERMINISTIC)) != 0u)
+    return M2RNN_ERROR_NOT_SUPPORTED;
+  const bool det = (flags & M2RNN_FLAG_DETERMINISTIC) != 0u;
+  const bool acc = (flags & M2RNN_FLAG_ACCUMULATE_Y) != 0u;
+  const bool bf = dt == M2RNN_DTYPE_BF16;
+  if (algo == M2RNN_ALGO_AUTO) {
+    algo = m2rnn_pick_algo(B, H, T, K, V, dt);
+    if (det && !atomic_free(algo, T, K, V, bf, acc) && is_long(algo))
+      algo = !m2rnn::mfma_supports(K, V, bf) ? M2RNN_ALGO_SIMPLE
+             : algo == M2RNN_ALGO_MFMA_LONG  ? M2RNN_ALGO_MFMA
+                                             : M2RNN_ALGO_MFMA_SPLIT;
+    if (det && !atomic_free(algo, T, K, V, bf, acc)) algo = M2RNN_ALGO_SIMPLE;
+  }
+  if (det && !atomic_free(algo, T, K, V, bf, acc)) return M2RNN_ERROR_NOT_SUPPORTED;
+  return M2RNN_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,18 +146,7 @@ m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const
   m2rnn_status st = check(k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
   if (seq_len && (reinterpret_cast<std::uintptr_t>(seq_len) & 3u) != 0) return M2RNN_ERROR_INVALID_VALUE;
-  if ((flags & ~static_cast<unsigned>(M2RNN_FLAG_ACCUMULATE_Y | M2RNN_FLAG_DETERMINISTIC)) != 0u)
-    return M2RNN_ERROR_NOT_SUPPORTED;
-  const bool det = (flags & M2RNN_FLAG_DETERMINISTIC) != 0u;
-  if (algo == M2RNN_ALGO_AUTO) {
-    algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
-    if (det && (algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT))
-      algo = algo == M2RNN_ALGO_MFMA_LONG ? M2RNN_ALGO_MFMA : M2RNN_ALGO_MFMA_SPLIT;
-  }
-  // the long kernels sum y over row tiles with atomic adds (T = 1 takes the
-  // decoding kernel, which does not)
-  if (det && T > 1 && (algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT))
-    return M2RNN_ERROR_NOT_SUPPORTED;
+  if ((st = resolve_algo(algo, B, H, T, K, V, in_dtype, flags)) != M2RNN_SUCCESS) return st;
   m2rnn::FwdArgs a{k, v, q, f, W, H0, y, H_T, B, H, T, K, V, in_dtype == M2RNN_DTYPE_BF16 ? 1 : 0,
                    (flags & M2RNN_FLAG_ACCUMULATE_Y) ? 1 : 0, seq_len, nullptr};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -283,14 +308,14 @@ m2rnn_status m2rnn_frontend(const void* x, const void* Wx, const float* bias, vo
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
 }
 
-m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
-                            m2rnn_algo algo, m2rnn_plan* plan) {
+m2rnn_status m2rnn_get_plan_ex(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                               m2rnn_algo algo, unsigned flags, m2rnn_plan* plan) {
   if (!plan) return M2RNN_ERROR_INVALID_VALUE;
   const void* p = reinterpret_cast<const void*>(static_cast<std::uintptr_t>(0x10000));
   const float* pf = static_cast<const float*>(p);
   m2rnn_status st = check(p, p, p, p, p, nullptr, pf, nullptr, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
-  if (algo == M2RNN_ALGO_AUTO) algo = m2rnn_pick_algo(B, H, T, K, V, in_dtype);
+  if ((st = resolve_algo(algo, B, H, T, K, V, in_dtype, flags)) != M2RNN_SUCCESS) return st;
   const bool mf = algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT;
   const bool lg = algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT;
   m2rnn::Plan pl = !(mf || lg) ? m2rnn::plan_simple(B, H, K, V)
@@ -306,6 +331,11 @@ m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dt
   plan->clears_y = pl.clears_y;
   plan->lds_bytes = pl.lds_bytes;
   return M2RNN_SUCCESS;
+}
+
+m2rnn_status m2rnn_get_plan(int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
+                            m2rnn_algo algo, m2rnn_plan* plan) {
+  return m2rnn_get_plan_ex(B, H, T, K, V, in_dtype, algo, 0u, plan);
 }
 
 const char* m2rnn_status_string(m2rnn_status status) {

@@ -52,6 +52,8 @@ hipError_t launch_simple(const FwdArgs& a, hipStream_t stream);
 // split: state operand as bf16 hi + lo (two MFMA passes) instead of one bf16.
 hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream);
 bool mfma_supports(int K, int V, int bf16);
+// workgroups the multi-step kernel gives one (b, h) unit (0: K not covered)
+int mfma_groups(int K);
 // One-step kernel (m2rnn_decode.hip): T == 1, no saved data, bf16, MFMA shapes.
 // launch_mfma routes such calls to it; it writes y itself (no clearing needed).
 bool decode_supports(const FwdArgs& a);

@@ -681,6 +681,11 @@ hipError_t fill_zero(float* p, long long n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+int mfma_groups(int K) {
+  const int nw = pick_nw(K);
+  return nw ? K / (16 * nw) : 0;
+}
+
 bool mfma_supports(int K, int V, int bf16) {
   if (!bf16) return false;
   if (V != 64 && V != 128) return false;

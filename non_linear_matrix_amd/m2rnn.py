@@ -35,12 +35,12 @@ class Plan(ctypes.Structure):
                 ("clears_y", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
 
 
-def get_plan(B: int, H: int, T: int, K: int, V: int, dtype: str, algo: str = "auto") -> dict:
-    """The launch plan the library would use (host only)."""
+def get_plan(B: int, H: int, T: int, K: int, V: int, dtype: str, algo: str = "auto", flags: int = 0) -> dict:
+    """The launch plan the library would use (host only); `flags` as m2rnn_fwd_ex's."""
     p = Plan()
-    st = load().m2rnn_get_plan(B, H, T, K, V, DTYPES[dtype], ALGOS[algo], ctypes.byref(p))
+    st = load().m2rnn_get_plan_ex(B, H, T, K, V, DTYPES[dtype], ALGOS[algo], flags, ctypes.byref(p))
     if st != 0:
-        raise M2RNNError(st, "m2rnn_get_plan")
+        raise M2RNNError(st, "m2rnn_get_plan_ex")
     d = {name: getattr(p, name) for name, _ in Plan._fields_}
     d["algo"] = {v: k for k, v in ALGOS.items()}[d["algo"]]
     return d
@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.m2rnn_status_string.restype = ctypes.c_char_p
     lib.m2rnn_get_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(Plan)]
     lib.m2rnn_get_plan.restype = i
+    lib.m2rnn_get_plan_ex.argtypes = [i, i, i, i, i, i, i, ctypes.c_uint, ctypes.POINTER(Plan)]
+    lib.m2rnn_get_plan_ex.restype = i
     u64 = ctypes.c_ulonglong
     lib.m2rnn_saved_bytes.argtypes = [i, i, i, i, i]
     lib.m2rnn_saved_bytes.restype = u64

@@ -110,6 +110,10 @@ def test_launch_plans():
     assert p["grid"] == 32 and p["groups_per_unit"] == 1 and p["clears_y"] == 0
     p = m2rnn.get_plan(1, 1, 64, 16, 16, "f32", "auto")
     assert p["algo"] == "simple" and p["grid"] == 1
+    # the latency-oriented kernel: one workgroup of V/32 waves per 16-row tile
+    p = m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "mfma_long")
+    assert p["grid"] == 32 * 8 and p["block"] == 256 and p["clears_y"] == 1
+    assert m2rnn.get_plan(2, 16, 32768, 64, 128, "bf16", "mfma_long_split")["grid"] == 32 * 4
     with pytest.raises(m2rnn.M2RNNError):
         m2rnn.get_plan(1, 1, 64, 20, 16, "f32", "auto")
 
@@ -151,6 +155,56 @@ def test_deterministic_flag_refuses_the_atomic_kernels():
         st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 2, 16, 64, 128, 1, m2rnn.ALGOS[algo],
                               det | m2rnn.FLAG_ACCUMULATE_Y, None)
         assert st == UNSUPPORTED, algo
+
+
+def test_deterministic_auto_resolves_to_a_covering_repeatable_kernel():
+    """AUTO under M2RNN_FLAG_DETERMINISTIC leaves the long kernel for the
+    multi-step split kernel only where that kernel covers the shape (else the
+    simple kernel), and never keeps a kernel that would add into y atomically
+    in an order-dependent way. Host only: the plan query launches nothing."""
+    det, acc = m2rnn.FLAG_DETERMINISTIC, m2rnn.FLAG_ACCUMULATE_Y
+    # K not covered by the multi-step kernel: the simple kernel (it once resolved
+    # to MFMA_SPLIT, which then refused the shape at launch)
+    for K in (48, 80, 96, 112):
+        assert m2rnn.get_plan(2, 3, 37, K, 128, "bf16", "auto", det)["algo"] == "simple", K
+    assert m2rnn.get_plan(2, 3, 37, 64, 128, "bf16", "auto", det)["algo"] == "mfma_split"
+    # one or two row tiles onto a cleared y stay on the long kernel
+    assert m2rnn.get_plan(2, 3, 37, 16, 128, "bf16", "auto", det)["algo"] == "mfma_long_split"
+    assert m2rnn.get_plan(2, 3, 37, 32, 128, "bf16", "auto", det)["algo"] == "mfma_long_split"
+    assert m2rnn.get_plan(2, 3, 37, 32, 128, "bf16", "auto", det | acc)["algo"] == "mfma_split"
+    # K = 128 on the multi-step kernel: two workgroups add into y
+    assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", det)["algo"] == "mfma_split"
+    assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", det | acc)["algo"] == "simple"
+    # without the flag nothing changes
+    assert m2rnn.get_plan(2, 3, 37, 48, 128, "bf16", "auto")["algo"] == "mfma_long_split"
+    assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", acc)["algo"] == "mfma_split"
+
+
+def test_deterministic_accumulate_refuses_two_atomic_groups():
+    """DETERMINISTIC | ACCUMULATE_Y on the multi-step kernels at K = 128 (two
+    workgroups add into a y that already holds values, and (y + a) + b need not
+    equal (y + b) + a) is refused before any launch; at K = 64 (one workgroup) and
+    for one step (the decoding kernel) it is accepted."""
+    lib = m2rnn.load()
+    det, acc = m2rnn.FLAG_DETERMINISTIC, m2rnn.FLAG_ACCUMULATE_Y
+    for algo in ("mfma", "mfma_split"):
+        st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 2, 2, 40, 128, 128, 1, m2rnn.ALGOS[algo], det | acc,
+                              None)
+        assert st == UNSUPPORTED, algo
+        with pytest.raises(m2rnn.M2RNNError):
+            m2rnn.get_plan(2, 2, 40, 128, 128, "bf16", algo, det | acc)
+        assert m2rnn.get_plan(2, 2, 40, 64, 128, "bf16", algo, det | acc)["algo"] == algo
+        assert m2rnn.get_plan(2, 2, 1, 128, 128, "bf16", algo, det | acc)["algo"] == algo
+        assert m2rnn.get_plan(2, 2, 40, 128, 128, "bf16", algo, det)["algo"] == algo
+    for algo in ("mfma_long", "mfma_long_split"):
+        with pytest.raises(m2rnn.M2RNNError):
+            m2rnn.get_plan(2, 2, 40, 48, 128, "bf16", algo, det)
+        assert m2rnn.get_plan(2, 2, 40, 32, 128, "bf16", algo, det)["algo"] == algo
+        with pytest.raises(m2rnn.M2RNNError):
+            m2rnn.get_plan(2, 2, 40, 32, 128, "bf16", algo, det | acc)
+    # unknown flag bits are refused by the plan query too
+    with pytest.raises(m2rnn.M2RNNError):
+        m2rnn.get_plan(2, 2, 40, 64, 128, "bf16", "auto", 4)
 
 
 def test_binding_refuses_host_tensors():

@@ -7,7 +7,7 @@ for the bf16-operand matrix-core path.
 import numpy as np
 import pytest
 
-from gpu_util import announce, gpu_run, nerr, oracle_units, pick, sample_units, to_device
+from gpu_util import announce, full_parity, gpu_run, nerr, oracle_units, to_device
 from non_linear_matrix_amd.inputs import CONFIGS, generate, scaled
 
 pytestmark = pytest.mark.gpu
@@ -40,38 +40,37 @@ def test_c1_fp32_full():
     assert nerr(y, yr) <= TOL_F32 and nerr(HT, HTr) <= TOL_F32
 
 
-SAMPLED = {
-    "C2": None,  # every unit
-    "C3": [(0, 0), (3, 7), (7, 15)],
-    "C4": [(0, 0), (0, 17), (0, 31)],
-    "C5": [(0, 0), (1, 15)],
-}
-
-
-# The single-bf16 operand (algo "mfma") meets the bar on C3 and C4 only: on C2 and
-# C5 some units amplify the per-step operand rounding past 2e-2 (reproduced by
-# a CPU emulation of the same arithmetic), which is what the split operand of
-# "mfma_split" (the default) is for.
-FULL = [(n, a) for n in ("C2", "C3", "C4", "C5") for a in ("mfma_split", "simple")] + \
-       [(n, "mfma") for n in ("C3", "C4")]
+# (workload, kernel family) pairs compared with the oracle on every (b, h) unit at
+# full size: every family AUTO or the benchmark runs there, and the fp32 simple
+# kernel. The latency-oriented families are in test_gpu_long.py.
+FULL = [("C2", "mfma_split"), ("C2", "simple"),
+        ("C3", "mfma"), ("C3", "mfma_split"), ("C3", "simple"),
+        ("C4", "mfma"), ("C4", "mfma_split"), ("C4", "simple"),
+        ("C5", "mfma_split"), ("C5", "simple")]
 
 
 @pytest.mark.parametrize("name,algo", FULL)
 def test_full_size_configs(name, algo):
-    """Full-size workloads in the launch configuration the benchmark times; the
-    oracle runs on sampled units (all units for C2)."""
-    cfg = CONFIGS[name]
-    units = SAMPLED[name]
-    announce(f"{name} full size, algo={algo}, sampled units={units}")
-    x = generate(cfg, 0)
-    y, HT = gpu_run(x, algo=algo)
-    assert np.all(np.isfinite(y)) and np.all(np.isfinite(HT))
-    yr, HTr = oracle_units(x, cfg.dtype, units)
-    if units is not None:
-        y, HT = pick(y, units), pick(HT, units)
-    ey, eh = nerr(y, yr), nerr(HT, HTr)
-    print(f"{name} {algo}: err y {ey:.3e} H_T {eh:.3e}", flush=True)
-    assert ey <= _tol(cfg, algo) and eh <= _tol(cfg, algo)
+    """Full-size workloads in the launch configuration the benchmark times,
+    every unit against the oracle."""
+    tol = _tol(CONFIGS[name], algo)
+    ey, eh = full_parity(name, algo, tol)
+    assert ey <= tol and eh <= tol
+
+
+# The single bf16 operand (MFMA, MFMA_LONG) meets the bar on C3 and C4, but on C2
+# and C5 (gates near 1 and inputs scaled by 1/sqrt(K), where the trajectory
+# amplifies per-step rounding) it goes past 2e-2; the split operand of the
+# default families is for those. The measured errors are recorded here so the
+# gap stays visible; the bound only says the result is still the same
+# trajectory to within a few percent.
+RECORDED_GAP = [("C2", "mfma"), ("C5", "mfma"), ("C2", "mfma_long"), ("C5", "mfma_long")]
+
+
+@pytest.mark.parametrize("name,algo", RECORDED_GAP)
+def test_single_operand_error_on_sensitive_workloads(name, algo):
+    ey, eh = full_parity(name, algo, TOL_BF16)
+    assert ey <= 0.1 and eh <= 0.1
 
 
 SHAPES = [(K, V) for K in (16, 32, 64, 128) for V in (16, 64, 128)] + [(48, 112), (96, 32)]
