@@ -56,7 +56,10 @@ typedef enum m2rnn_status {
   M2RNN_SUCCESS = 0,
   M2RNN_ERROR_INVALID_VALUE = 1,
   M2RNN_ERROR_NOT_SUPPORTED = 2,
-  M2RNN_ERROR_LAUNCH = 3
+  M2RNN_ERROR_LAUNCH = 3,
+  /* m2rnn_bwd_noalloc only: the shape needs more workspace than the
+   * library-owned scratch array holds (64 MiB per GPU) */
+  M2RNN_ERROR_SCRATCH_TOO_SMALL = 4
 } m2rnn_status;
 
 typedef enum m2rnn_dtype {
@@ -209,6 +212,27 @@ m2rnn_status m2rnn_bwd_algo(const void* k, const void* v, const void* q, const v
                             void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                             m2rnn_algo algo, void* stream);
 
+/* m2rnn_bwd_algo for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * arguments are m2rnn_bwd_algo's without `workspace`: the workspace lives in a
+ * device array inside the library, 64 MiB per GPU, which each GPU holds from its
+ * first use until the process ends. The call allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine); the caller still passes every
+ * input and output. Its first call on a device resolves the array's address on
+ * that device (do it once before capturing a graph). Results are bitwise those
+ * of m2rnn_bwd_algo with the same arguments.
+ * All calls on one GPU share its array: calls that overlap on one GPU (other
+ * streams, other host threads) race and give undefined results; calls ordered
+ * on one stream are safe (each call writes every part of the array it reads).
+ * Errors as m2rnn_bwd_algo, plus M2RNN_ERROR_SCRATCH_TOO_SMALL, returned before
+ * any HIP call, when m2rnn_bwd_workspace_bytes(B, H, T, K, V) exceeds 64 MiB
+ * (for example B H T K V above about 29 million elements at K = V = 128). */
+m2rnn_status m2rnn_bwd_noalloc(const void* k, const void* v, const void* q, const void* f, const void* W,
+                               const float* H0, const void* saved, const float* dy, const float* dH_T,
+                               float* dk, float* dv, float* dq, float* df, float* dW, float* dH0,
+                               int B, int H, int T, int K, int V, m2rnn_dtype in_dtype, m2rnn_algo algo,
+                               void* stream);
+
 /* ---- Training with recomputation (zh summary §2.2, parallelism paragraph: the
  * backward pass recomputes the forward states rather than keeping them all).
  * The sequence is cut into segments of `segment` steps (the last one may be
@@ -319,7 +343,8 @@ const char* m2rnn_status_string(m2rnn_status status);
 /* Library ABI version: major * 10000 + minor * 100 + patch (0.2.0 added
  * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones and the front-end, 0.4.0 MFMA_LONG, 0.5.0 AUTO's
  * choice of MFMA_LONG_SPLIT and M2RNN_FLAG_DETERMINISTIC, 0.6.0 MFMA_LONG* in
- * the training forwards and m2rnn_bwd_algo). */
+ * the training forwards and m2rnn_bwd_algo, 0.7.0 m2rnn_get_plan_ex and
+ * m2rnn_bwd_noalloc). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

@@ -208,23 +208,68 @@ unsigned long long m2rnn_bwd_workspace_bytes(int B, int H, int T, int K, int V) 
   return static_cast<unsigned long long>(m2rnn::bwd_workspace_bytes(B, H, T, K, V));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation of a backward call (everything but the workspace), then the launch
+// with the given workspace.
+m2rnn_status bwd_check(const void* k, const void* v, const void* q, const void* f, const void* W,
+                       const float* H0, const void* saved, const float* dy, const float* dH_T, float* dk,
+                       float* dv, float* dq, float* df, float* dW, float* dH0, int B, int H, int T, int K, int V,
+                       m2rnn_dtype in_dtype, m2rnn_algo& algo) {
+  // the forward's argument rules, with dy standing in for y
+  m2rnn_status st = check(k, v, q, f, W, H0, dy, dH_T, B, H, T, K, V, in_dtype, M2RNN_ALGO_MFMA);
+  if (st != M2RNN_SUCCESS) return st;
+  if ((st = training_algo(algo, B, H, T, K, V, in_dtype)) != M2RNN_SUCCESS) return st;
+  if (!saved || !dk || !dv || !dq || !df || !dW) return M2RNN_ERROR_INVALID_VALUE;
+  if (!aligned16(saved) || !aligned16(dk) || !aligned16(dv) || !aligned16(dq) || !aligned16(df) ||
+      !aligned16(dW) || (dH0 && !aligned16(dH0)))
+    return M2RNN_ERROR_INVALID_VALUE;
+  return M2RNN_SUCCESS;
+}
+
+m2rnn_status bwd_launch(const void* k, const void* v, const void* q, const void* f, const void* W,
+                        const void* saved, const float* dy, const float* dH_T, float* dk, float* dv, float* dq,
+                        float* df, float* dW, float* dH0, void* workspace, int B, int H, int T, int K, int V,
+                        m2rnn_algo algo, void* stream) {
+  m2rnn::BwdLaunch p{k, v, q, f, W, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V,
+                     0, 0, 0, is_long(algo) ? 1 : 0};
+  hipError_t e = m2rnn::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
 m2rnn_status m2rnn_bwd_algo(const void* k, const void* v, const void* q, const void* f, const void* W,
                             const float* H0, const void* saved, const float* dy, const float* dH_T,
                             float* dk, float* dv, float* dq, float* df, float* dW, float* dH0,
                             void* workspace, int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
                             m2rnn_algo algo, void* stream) {
-  // the forward's argument rules, with dy standing in for y
-  m2rnn_status st = check(k, v, q, f, W, H0, dy, dH_T, B, H, T, K, V, in_dtype, M2RNN_ALGO_MFMA);
+  m2rnn_status st = bwd_check(k, v, q, f, W, H0, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, B, H, T, K, V,
+                              in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
-  if ((st = training_algo(algo, B, H, T, K, V, in_dtype)) != M2RNN_SUCCESS) return st;
-  if (!saved || !dk || !dv || !dq || !df || !dW || !workspace) return M2RNN_ERROR_INVALID_VALUE;
-  if (!aligned16(saved) || !aligned16(dk) || !aligned16(dv) || !aligned16(dq) || !aligned16(df) ||
-      !aligned16(dW) || !aligned16(workspace) || (dH0 && !aligned16(dH0)))
-    return M2RNN_ERROR_INVALID_VALUE;
-  m2rnn::BwdLaunch p{k, v, q, f, W, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V,
-                     0, 0, 0, is_long(algo) ? 1 : 0};
-  hipError_t e = m2rnn::launch_bwd(p, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
+  if (!workspace || !aligned16(workspace)) return M2RNN_ERROR_INVALID_VALUE;
+  return bwd_launch(k, v, q, f, W, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, workspace, B, H, T, K, V, algo,
+                    stream);
+}
+
+m2rnn_status m2rnn_bwd_noalloc(const void* k, const void* v, const void* q, const void* f, const void* W,
+                               const float* H0, const void* saved, const float* dy, const float* dH_T,
+                               float* dk, float* dv, float* dq, float* df, float* dW, float* dH0,
+                               int B, int H, int T, int K, int V, m2rnn_dtype in_dtype, m2rnn_algo algo,
+                               void* stream) {
+  m2rnn_status st = bwd_check(k, v, q, f, W, H0, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, B, H, T, K, V,
+                              in_dtype, algo);
+  if (st != M2RNN_SUCCESS) return st;
+  // refused before any HIP call when the library's array cannot hold the workspace
+  if (m2rnn::bwd_workspace_bytes(B, H, T, K, V) > m2rnn::noalloc_scratch_bytes())
+    return M2RNN_ERROR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  if (m2rnn::noalloc_scratch(&ws) != hipSuccess) return M2RNN_ERROR_LAUNCH;
+  return bwd_launch(k, v, q, f, W, saved, dy, dH_T, dk, dv, dq, df, dW, dH0, ws, B, H, T, K, V, algo, stream);
 }
 
 m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* f, const void* W,
@@ -349,11 +394,14 @@ const char* m2rnn_status_string(m2rnn_status status) {
              "or an algorithm that does not cover the shape)";
     case M2RNN_ERROR_LAUNCH:
       return "kernel launch failed";
+    case M2RNN_ERROR_SCRATCH_TOO_SMALL:
+      return "the workspace this shape needs exceeds the library-owned scratch array "
+             "(m2rnn_bwd_noalloc: 64 MiB per GPU)";
     default:
       return "unknown status";
   }
 }
 
-int m2rnn_version(void) { return 600; }
+int m2rnn_version(void) { return 700; }
 
 }  // extern "C"

@@ -83,6 +83,12 @@ long long bwd_long_partial_bytes(int B, int H, int T, int K, int V);
 // dW kernels are launch_bwd's)
 hipError_t launch_bwd_long(const BwdLaunch& p, char* dA_out, float* partials, hipStream_t stream);
 
+// The library-owned backward workspace of m2rnn_bwd_noalloc (m2rnn_noalloc.hip):
+// its size, and its device address on the current device (resolved on the first
+// call per device; no allocation).
+long long noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
+
 // Training with recomputation over segments of S steps (m2rnn_ckpt.cpp).
 long long ckpt_bytes(int B, int H, int T, int K, int V, int S);
 long long bwd_recompute_workspace_bytes(int B, int H, int T, int K, int V, int S);

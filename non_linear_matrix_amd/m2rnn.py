@@ -12,7 +12,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "LIB_PATH", "M2RNNError", "load", "fwd", "check_args", "pick_algo", "status_string", "version",
-    "fwd_save", "bwd", "saved_bytes", "bwd_workspace_bytes",
+    "fwd_save", "bwd", "bwd_noalloc", "saved_bytes", "bwd_workspace_bytes",
     "STATUS", "ALGOS", "DTYPES", "declared_functions", "get_plan", "Plan", "FLAG_ACCUMULATE_Y",
     "FLAG_DETERMINISTIC",
 ]
@@ -20,7 +20,8 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm2rnn.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "m2rnn.h")
 
-STATUS = {0: "M2RNN_SUCCESS", 1: "M2RNN_ERROR_INVALID_VALUE", 2: "M2RNN_ERROR_NOT_SUPPORTED", 3: "M2RNN_ERROR_LAUNCH"}
+STATUS = {0: "M2RNN_SUCCESS", 1: "M2RNN_ERROR_INVALID_VALUE", 2: "M2RNN_ERROR_NOT_SUPPORTED", 3: "M2RNN_ERROR_LAUNCH",
+          4: "M2RNN_ERROR_SCRATCH_TOO_SMALL"}
 ALGOS = {"auto": 0, "simple": 1, "mfma": 2, "mfma_split": 3, "mfma_long": 4, "mfma_long_split": 5}
 DTYPES = {"f32": 0, "bf16": 1}
 FLAG_ACCUMULATE_Y = 1
@@ -91,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.m2rnn_bwd.restype = i
     lib.m2rnn_bwd_algo.argtypes = lib.m2rnn_bwd.argtypes[:-1] + [i, vp]
     lib.m2rnn_bwd_algo.restype = i
+    lib.m2rnn_bwd_noalloc.argtypes = lib.m2rnn_bwd.argtypes[:15] + [i, i, i, i, i, i, i, vp]
+    lib.m2rnn_bwd_noalloc.restype = i
     lib.m2rnn_frontend.argtypes = [vp, vp, fp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.m2rnn_frontend.restype = i
     lib.m2rnn_ckpt_bytes.argtypes = [i, i, i, i, i, i]
@@ -292,6 +295,29 @@ def bwd(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, out=N
     if st != 0:
         raise M2RNNError(st, "m2rnn_bwd_algo")
     out["workspace"] = ws  # keep alive until the stream has run
+    return out
+
+
+def bwd_noalloc(k, v, q, f, W, H0, saved, dy, dH_T=None, *, want_dH0: bool = True, out=None, stream=None,
+                algo: str = "auto") -> dict:
+    """Backward pass with the library's own workspace (m2rnn_bwd_noalloc): as
+    bwd(), for shapes whose workspace fits the library's 64 MiB array."""
+    import torch
+
+    lib = load()
+    B, H, T, K = k.shape
+    V = v.shape[-1]
+    _check_dy(dy, dH_T, B, H, T, K, V)
+    if out is None:
+        out = _grad_buffers(B, H, T, K, V, k.device, want_dH0)
+    if stream is None:
+        stream = torch.cuda.current_stream(k.device)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.m2rnn_bwd_noalloc(ptr(k), ptr(v), ptr(q), ptr(f), ptr(W), ptr(H0), ptr(saved), ptr(dy), ptr(dH_T),
+                               ptr(out["dk"]), ptr(out["dv"]), ptr(out["dq"]), ptr(out["df"]), ptr(out["dW"]),
+                               ptr(out["dH0"]), B, H, T, K, V, DTYPES["bf16"], ALGOS[algo], stream.cuda_stream)
+    if st != 0:
+        raise M2RNNError(st, "m2rnn_bwd_noalloc")
     return out
 
 

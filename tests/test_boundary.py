@@ -28,7 +28,7 @@ def _check(**over):
 def test_library_exists_and_loads():
     assert os.path.exists(m2rnn.LIB_PATH), "build the library first (python -m non_linear_matrix_amd.build)"
     lib = m2rnn.load()
-    assert m2rnn.version() == 600
+    assert m2rnn.version() == 700
 
 
 def test_every_declared_symbol_is_exported():
@@ -45,11 +45,11 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_cover_every_code():
     seen = set()
-    for code in (0, 1, 2, 3):
+    for code in (0, 1, 2, 3, 4):
         s = m2rnn.status_string(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 4
+    assert len(seen) == 5
     assert m2rnn.status_string(99) == "unknown status"
 
 
@@ -205,6 +205,24 @@ def test_deterministic_accumulate_refuses_two_atomic_groups():
     # unknown flag bits are refused by the plan query too
     with pytest.raises(m2rnn.M2RNNError):
         m2rnn.get_plan(2, 2, 40, 64, 128, "bf16", "auto", 4)
+
+
+def test_noalloc_backward_refuses_a_shape_beyond_its_array():
+    """m2rnn_bwd_noalloc: a workspace above the library's 64 MiB array is refused
+    with its own status before any HIP call; invalid arguments keep the usual
+    codes."""
+    lib = m2rnn.load()
+    bf, auto = m2rnn.DTYPES["bf16"], m2rnn.ALGOS["auto"]
+    B, H, T, K, V = 8, 16, 2048, 128, 128
+    assert m2rnn.bwd_workspace_bytes(B, H, T, K, V) > 64 << 20
+    st = lib.m2rnn_bwd_noalloc(A, A, A, A, A, None, A, A, None, A, A, A, A, A, None, B, H, T, K, V, bf, auto, None)
+    assert st == 4 and "scratch" in m2rnn.status_string(st)
+    st = lib.m2rnn_bwd_noalloc(A, A, A, A, A, None, None, A, None, A, A, A, A, A, None, 1, 2, 40, 64, 128, bf,
+                               auto, None)
+    assert st == INVALID  # no saved buffer
+    st = lib.m2rnn_bwd_noalloc(A, A, A, A, A, None, A, A, None, A, A, A, A, A, None, 1, 2, 40, 48, 128, bf,
+                               m2rnn.ALGOS["mfma"], None)
+    assert st == UNSUPPORTED  # K = 48 has no backward kernel
 
 
 def test_binding_refuses_host_tensors():
