@@ -82,7 +82,7 @@ __device__ __forceinline__ unsigned int pack_bf16(float x0, float x1) {
   return __builtin_bit_cast(unsigned int, __builtin_convertvector(f2{x0, x1}, bf16x2));
 }
 
-template <int V, int NW>
+template <int V, int NW, bool SPLIT>
 struct Layout {
   static constexpr int R = 16 * NW;   // rows per workgroup
   static constexpr int CT = V / 16;   // 16-column tiles
@@ -93,18 +93,24 @@ struct Layout {
   // conflict-free across a row group
   static constexpr int NVX = 2 * CT + 4;
   static constexpr int HROW = V + 8;  // bf16 per LDS state row (padded)
+  // floats per row of the partial readouts: the 4-float pad puts the 16 rows a
+  // publishing 16-lane group writes on distinct banks (unpadded, all 16 hit the same)
+  static constexpr int YROW = V + 4;
   // stage buffers: chunk c+1 goes into chunk c-1's buffer early in chunk c, once
   // the readout of chunk c-1's last steps (step 0 of chunk c) is behind a barrier
   static constexpr int NSB = 2;
-  static constexpr int NHS = 4;       // state-tile slots per wave (readout lags one step pair)
+  // state-tile slots per wave: a step pair's readout operands are read at the
+  // start of the next pair, before its first step overwrites the older slot
+  static constexpr int NHS = 2;
+  static constexpr int NPL = SPLIT ? 2 : 1;  // planes per slot: bf16 hi (and lo with SPLIT)
   static constexpr int THREADS = 64 * NW;
   // LDS regions (bytes)
   static constexpr int KX_BYTES = NSB * kChunk * R * 4;          // (hi, lo) of c k, bf16 pair
   static constexpr int VX_BYTES = NSB * kChunk * 16 * NVX * 4;   // rank-1 A operands, [s][m][.]
   static constexpr int QS_BYTES = NSB * kChunk * R * 2;          // q, bf16
   static constexpr int FS_BYTES = NSB * kChunk * 4 * 4;          // f, a, -2a, pad
-  static constexpr int HB_BYTES = NW * NHS * 16 * HROW * 2;      // per-wave state tiles
-  static constexpr int YP_BYTES = NW * kChunk * V * 4;           // per-wave partial readouts
+  static constexpr int HB_BYTES = NW * NHS * NPL * 16 * HROW * 2;  // per-wave state tiles
+  static constexpr int YP_BYTES = NW * kChunk * YROW * 4;        // per-wave partial readouts
   static constexpr int Z_BYTES = 16;                             // zeros
   static constexpr int KX_OFF = 0;
   static constexpr int VX_OFF = KX_OFF + KX_BYTES;
@@ -113,7 +119,10 @@ struct Layout {
   static constexpr int HB_OFF = FS_OFF + FS_BYTES;
   static constexpr int YP_OFF = HB_OFF + HB_BYTES;
   static constexpr int Z_OFF = YP_OFF + YP_BYTES;
-  static constexpr int TOTAL = Z_OFF + Z_BYTES;
+  // before the loop the head's W (V padded rows) is staged from HB_OFF on, over
+  // the state tiles and, if they are smaller, the partial readouts
+  static constexpr int W_STAGE_BYTES = V * HROW * 2;
+  static constexpr int TOTAL = (Z_OFF + Z_BYTES > HB_OFF + W_STAGE_BYTES) ? Z_OFF + Z_BYTES : HB_OFF + W_STAGE_BYTES;
   // 16-byte global load slots per chunk
   static constexpr int SLOT_K = kChunk * R / 8;
   static constexpr int SLOT_Q = kChunk * R / 8;
@@ -124,9 +133,9 @@ struct Layout {
 };
 
 // Chunk staging: each thread owns up to SLOTS_PER_THREAD 16-byte global slots.
-template <int V, int NW>
+template <int V, int NW, bool SPLIT>
 struct Stager {
-  using L = Layout<V, NW>;
+  using L = Layout<V, NW, SPLIT>;
   u4 reg[L::SLOTS_PER_THREAD];
   unsigned short freg;  // one gate value (threads < kChunk)
 
@@ -246,31 +255,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Issue order for one pipeline phase: each matrix instruction followed by NV
-// vector-ALU instructions, so the matrix core works while the wave issues the
-// epilogue (a wave issues in order: back-to-back MFMAs leave the VALU idle).
-template <int NM, int NV>
-__device__ __forceinline__ void interleave_mfma() {
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // NV VALU
-  }
-}
-// VALU instructions after each MFMA (measured on C3: phase 0 has 14 MFMAs, the
-// readout phase 16, the others 8, against ~44 VALU of epilogue each)
-constexpr int kNvPhase0 = 3, kNvReadout = 2, kNvPhase = 5;
-// the same for the two-pass variant (twice the product MFMAs)
-constexpr int kNvPhase0Split = 1, kNvReadoutSplit = 1, kNvPhaseSplit = 3;
-
 __device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 template <int V, int NW, bool SPLIT, bool SAVE>
 __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
-  using L = Layout<V, NW>;
+  using L = Layout<V, NW, SPLIT>;
   constexpr int R = L::R, CT = L::CT, KB = L::KB, HROW = L::HROW, NVX = L::NVX, NSB = L::NSB, NHS = L::NHS;
+  constexpr int NPL = L::NPL;
   static_assert(KB >= 2 && CT == 2 * KB, "V must be a multiple of 32, at least 64");
   __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
 
@@ -290,13 +283,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   unsigned int* vx_all = reinterpret_cast<unsigned int*>(lds + L::VX_OFF);
   const unsigned short* qs_all = reinterpret_cast<const unsigned short*>(lds + L::QS_OFF);
   const float* fs_all = reinterpret_cast<const float*>(lds + L::FS_OFF);
-  unsigned short* hb_w = reinterpret_cast<unsigned short*>(lds + L::HB_OFF) + w * NHS * 16 * HROW;
+  unsigned short* hb_w = reinterpret_cast<unsigned short*>(lds + L::HB_OFF) + w * NHS * NPL * 16 * HROW;
   float* yp_all = reinterpret_cast<float*>(lds + L::YP_OFF);
   const unsigned int* zero_lds = reinterpret_cast<const unsigned int*>(lds + L::Z_OFF);
 
   // ---- prologue. Every global read of the prologue (W, H0, chunks 0 and 1) is
   // issued before the first wait, so their latencies overlap.
-  Stager<V, NW> st, st1;
+  Stager<V, NW, SPLIT> st, st1;
   const int nchunks = (Tb + kChunk - 1) / kChunk;
   st.load(a, unit, row0, 0, Tb);
   if (nchunks > 1) st1.load(a, unit, row0, 1, Tb);
@@ -321,7 +314,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   bf16x8 Wf[CT][KB];
   {
     constexpr int WROW = HROW;  // padded row, as the state tiles
-    static_assert(V * WROW * 2 <= L::HB_BYTES, "W fits in the state-tile region");
+    static_assert(L::HB_OFF + V * WROW * 2 <= L::TOTAL, "W fits in the staging region");
     unsigned short* wst = reinterpret_cast<unsigned short*>(lds + L::HB_OFF);
 #pragma unroll
     for (int p = 0; p < WLOADS; ++p) {
@@ -391,7 +384,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   // rank-1 write of a step as the initial accumulator: acc[c] = (v, tile c) x (hi, lo of c k).
   struct R1 {
     unsigned int kpair;
-    u4 win[CT / 2];  // tile pair k: (v pair of tile 2k, of tile 2k+1, 0, 0)
+    uint2 win[CT / 2];  // tile pair k: (v pair of tile 2k, v pair of tile 2k+1)
   };
   auto rank1_load = [&](const Buf& B, int s) {
     R1 r;
@@ -399,16 +392,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     r.kpair = *kp;
     const unsigned int* vp = B.vx + (s * 16 + n) * NVX;
 #pragma unroll
-    for (int k = 0; k < CT / 2; ++k) r.win[k] = *reinterpret_cast<const u4*>(vp + 4 * k);
+    for (int k = 0; k < CT / 2; ++k) r.win[k] = *reinterpret_cast<const uint2*>(vp + 4 * k);
     return r;
-  };
-  auto rank1_init = [&](const R1& r, f4 (&acc)[CT]) {
-    const u4 bx0 = u4{r.kpair, 0u, 0u, 0u};
-    const u4 bx1 = u4{0u, r.kpair, 0u, 0u};
-#pragma unroll
-    for (int c = 0; c < CT; ++c)
-      acc[c] = mfma(__builtin_bit_cast(bf16x8, r.win[c / 2]), __builtin_bit_cast(bf16x8, (c & 1) ? bx1 : bx0),
-                    f4{0, 0, 0, 0});
   };
 
   // readout partials: Dr[P] lane (g, n) accumulates y_{t0 + n}[position 16 P + 4 g + i]
@@ -417,26 +402,47 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int p = 0; p < CT; ++p) Dr[p] = f4{0, 0, 0, 0};
 
-  // readout of the steps s0, s0 + 1 (s0 even) of the chunk in B, state tiles in
-  // slots s0 & 3 and (s0 + 1) & 3; step s0 + p contributes only if p < nvalid
-  auto readout = [&](const Buf& B, int s0, int nvalid) {
+  // Readout of a step pair (s0, s0 + 1), s0 even, on step s0 + 2: the transposed
+  // state tiles of both steps (slots s0 & 1 and (s0 + 1) & 1; with SPLIT the low
+  // halves too) and q, read half the tiles at a time a phase before their MFMAs.
+  // The step writes its own state tiles at its end, after these reads.
+  constexpr int HT = CT / 2;  // tiles per readout half
+  struct RO {
+    bf16x8 a[NPL][HT];  // A operand per plane (hi, lo) and 16-column tile of the half
+  };
+  auto readout_q = [&](const Buf& B, int s0, int nvalid) {
     const int p = g / 2;                 // which step of the pair this lane group carries
     const int rr = 8 * (g % 2);          // first of its 8 rows
     const int s = s0 + p;
     s8 qv = *reinterpret_cast<const s8*>(B.qs + s * R + 16 * w + rr);
     if (n != s || p >= nvalid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
-    const bf16x8 Bq = __builtin_bit_cast(bf16x8, qv);
-    // source lane (g, n): row rr + n/4 (+4) of the step's slot, positions 16 P + 4 (n % 4)
-    const unsigned short* src = hb_w + (s & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
-#pragma unroll
-    for (int P = 0; P < CT; ++P) {
-      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * P));
-      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s4*)(src + 16 * P + 4 * HROW));
-      const s8 av = s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      Dr[P] = mfma(__builtin_bit_cast(bf16x8, av), Bq, Dr[P]);
-    }
+    return __builtin_bit_cast(bf16x8, qv);  // q_{s0 + p} in column s0 + p (p < nvalid), zero elsewhere
   };
+  auto readout_load = [&](int s0, int half) {
+    RO ro;
+    const int p = g / 2, rr = 8 * (g % 2), s = s0 + p;
+#pragma unroll
+    for (int pl = 0; pl < NPL; ++pl) {
+      // source lane (g, n): row rr + n/4 (+4) of the step's slot, positions 16 P + 4 (n % 4)
+      const unsigned short* src =
+          hb_w + ((s & (NHS - 1)) * NPL + pl) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
+#pragma unroll
+      for (int i = 0; i < HT; ++i) {
+        const int P = half * HT + i;
+        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * P));
+        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(src + 16 * P + 4 * HROW));
+        ro.a[pl][i] = __builtin_bit_cast(bf16x8, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+    }
+    return ro;
+  };
+  // readout MFMA j (< NPL HT) of a half
+  auto readout_mma = [&](const RO& ro, const bf16x8& bq, int half, int j) {
+    const int pl = j / HT, i = j % HT;
+    Dr[half * HT + i] = mfma(ro.a[pl][i], bq, Dr[half * HT + i]);
+  };
+  constexpr int NRH = NPL * HT;  // readout MFMAs per half
 
   float* y = a.y;
   const bool atomic_y = splits > 1 || a.accumulate;
@@ -444,9 +450,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   // y for the steps t0 .. t0 + nsteps - 1 of one chunk from the summed partials
   auto ysum_group = [&](int t0, int grp) {
     const int sn = grp / (V / 4), pos = 4 * (grp % (V / 4));
-    f4 sum = *reinterpret_cast<const f4*>(yp_all + sn * V + pos);
+    f4 sum = *reinterpret_cast<const f4*>(yp_all + sn * L::YROW + pos);
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(yp_all + (ww * kChunk + sn) * V + pos);
+    for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(yp_all + (ww * kChunk + sn) * L::YROW + pos);
     sum *= kInvC;
     // position 16 P + 4 gg  ->  column 32 (P/2) + 16 (gg%2) + 8 (P%2) + 4 (gg/2)
     const int P = pos / 16, gg = (pos % 16) / 4;
@@ -463,22 +469,23 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 
   // Chunk end, spread over the first steps of the next chunk so that its LDS
   // round trips overlap with their compute:
-  //   step 0 (end): publish the waves' partial readouts of the finished chunk
-  //                 (Dr, which that step's readout has just completed); LDS barrier
-  //   step 1:       stage the next chunk from the registers loaded a chunk ago,
+  //   step 1 (end): publish the waves' partial readouts of the finished chunk
+  //                 (Dr, which the readout MFMAs of steps 0 and 1 have just
+  //                 completed with the chunk's last pair); LDS barrier
+  //   step 2:       stage the next chunk from the registers loaded a chunk ago,
   //                 then fetch the one after it
-  //   steps 2..:    sum the partials into y, one group per step and thread
+  //   steps 3..:    sum the partials into y, one group per step and thread
   //   step kSync:   LDS barrier: the staged chunk is visible before the step
   //                 that first prefetches from it (step 14), and every wave has
   //                 summed before the next chunk end overwrites the partials
   constexpr int kGroups = kChunk * (V / 4) / L::THREADS;  // y-sum groups per thread
   static_assert(kGroups * L::THREADS == kChunk * (V / 4), "whole groups per thread");
-  constexpr int kSync = 8;
-  static_assert(2 + kGroups <= kSync && kSync < kChunk - 2, "chunk-end schedule");
+  constexpr int kSum0 = 3, kSync = 8;
+  static_assert(kSum0 + kGroups <= kSync && kSync < kChunk - 2, "chunk-end schedule");
   auto publish = [&]() {
-    float* ypw = yp_all + w * kChunk * V;
+    float* ypw = yp_all + w * kChunk * L::YROW;
 #pragma unroll
-    for (int P = 0; P < CT; ++P) *reinterpret_cast<f4*>(ypw + n * V + 16 * P + 4 * g) = Dr[P];
+    for (int P = 0; P < CT; ++P) *reinterpret_cast<f4*>(ypw + n * L::YROW + 16 * P + 4 * g) = Dr[P];
 #pragma unroll
     for (int P = 0; P < CT; ++P) Dr[P] = f4{0, 0, 0, 0};
     lds_barrier();
@@ -490,17 +497,42 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     }
   };
   auto chunk_end_work = [&](int s, int c) {
-    if (s == 0) publish();
-    if (s == 1) stage_next(c + 1);
-    if (s >= 2 && s < 2 + kGroups) ysum_group((c - 1) * kChunk, tid + (s - 2) * L::THREADS);
+    if (s == 1) publish();
+    if (s == 2) stage_next(c + 1);
+    if (s >= kSum0 && s < kSum0 + kGroups) ysum_group((c - 1) * kChunk, tid + (s - kSum0) * L::THREADS);
     if (s == kSync) lds_barrier();
   };
 
-  // epilogue of state tiles 2b, 2b+1: tanh via exp2/rcp, gate blend, next operand
-  // block, rounded tile to the readout slot
-  auto epilogue = [&](int b, const f4 (&cur)[CT], float fg, float av, float m2a, unsigned short* hdst, int t) {
+  // one state element, tile c, register i, in two parts so that consecutive
+  // groups overlap: r = 1 / (1 + exp2(u)) (tanh(x) = 1 - 2 r), then the gate
+  // blend G <- f G + a - 2 a r; the blend of an element runs in the group after
+  // its reciprocal, so no blend waits on a transcendental result
+  auto elem_r = [&](const f4 (&cur)[CT], int c, int i) {
+    const float e = __builtin_amdgcn_exp2f(cur[c][i]);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+  };
+  auto elem_g = [&](int c, int i, float r, float fg, float av, float m2a) {
+    G[c][i] = fmaf(m2a, r, fmaf(fg, G[c][i], av));
+  };
+  // the operand block b for the next product from the new tiles 2b, 2b + 1
+  auto block_out = [&](int b, int t) {
+    make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
     if constexpr (SAVE) {
-      // the pre-activation c A_t of tiles 2b, 2b+1, as bf16
+      if (t < T) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, t + 1, T, a.K, V) + rt_off + b * 1024) = Bf[b];
+    }
+  };
+  // the step's rounded state tiles to its readout slot(s), at the step's end
+  auto tiles_out = [&](int s) {
+    unsigned short* hdst = hb_w + (s & (NHS - 1)) * NPL * 16 * HROW + n * HROW + 8 * g;
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
+      if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(hdst + 16 * HROW + 32 * b) = Bl[b];
+    }
+  };
+  // training forward: the pre-activation c A_t of tiles 2b, 2b+1, as bf16
+  auto save_pre = [&](int b, const f4 (&cur)[CT], int t) {
+    if constexpr (SAVE) {
       if (t < T) {
         const f4 u0 = cur[2 * b], u1 = cur[2 * b + 1];
         const u4 pk = u4{pack_bf16(u0[0], u0[1]), pack_bf16(u0[2], u0[3]), pack_bf16(u1[0], u1[1]),
@@ -508,86 +540,147 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
         *reinterpret_cast<u4*>(saved + saved_pre_off(unit, t, a.B, a.H, T, a.K, V) + rt_off + b * 1024) = pk;
       }
     }
-#pragma unroll
-    for (int c = 2 * b; c < 2 * b + 2; ++c) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(cur[c][i]);
-        const float r = __builtin_amdgcn_rcpf(1.0f + e);
-        G[c][i] = fmaf(m2a, r, fmaf(fg, G[c][i], av));
-      }
-    }
-    make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
-    *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
-    if constexpr (SAVE) {
-      if (t < T) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, t + 1, T, a.K, V) + rt_off + b * 1024) = Bf[b];
-    }
   };
 
-  auto products = [&](int b, int c_lo, int c_hi, f4 (&acc)[CT]) {
-#pragma unroll
-    for (int c = c_lo; c < c_hi; ++c) {
-      acc[c] = mfma(Wf[c][b], Bf[b], acc[c]);
-      if constexpr (SPLIT) acc[c] = mfma(Wf[c][b], Bl[b], acc[c]);
-    }
+  // product of operand block b into tile c (two passes with SPLIT)
+  auto prod = [&](int b, int c, f4 (&acc)[CT]) {
+    acc[c] = mfma(Wf[c][b], Bf[b], acc[c]);
+    if constexpr (SPLIT) acc[c] = mfma(Wf[c][b], Bl[b], acc[c]);
+  };
+  // rank-1 write c k v^T of a step into tile c as the accumulator's start
+  // (16x16x16: the pair (v, v) of the tile against (hi, lo) of c k)
+  auto rank1_tile = [&](const R1& r, int c, f4 (&acc)[CT]) {
+    const s4 av4 = __builtin_bit_cast(s4, r.win[c / 2]);
+    const s4 bk = __builtin_bit_cast(s4, (c & 1) ? uint2{0u, r.kpair} : uint2{r.kpair, 0u});
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av4, bk, f4{0, 0, 0, 0}, 0, 0, 0);
   };
 
   // per-step operands fetched ahead: the gate scalars of the next step and the
   // rank-1 operands of the step after it
   struct Pre {
-    f4 fs;
+    float2 fs;  // f and a = (1 - f) c (every loaded component is used: no load's register is reused early)
     R1 r1;
+  };
+
+  // Matrix-core work of phase p of a step (p < KB; phase p runs the epilogue of
+  // tiles 2p, 2p + 1), in issue order; a product is two MFMAs with SPLIT:
+  //   the last block's products for tiles 2p + 2, 2p + 3 of this step (cur),
+  //   phase 0: the next step's rank-1 writes (nxt); phase p > 0: operand block
+  //   p - 1 into every tile of the next step (nxt),
+  //   on even steps the previous pair's readout: half of it in phase 1, the other
+  //   half in phase 3 (both in phase 1 when V = 64);
+  // and at the step's end the last block's products for tiles 0, 1 (nxt). Each
+  // tile's epilogue comes a phase after its last product.
+  constexpr int NPU = SPLIT ? 2 : 1;  // MFMAs per product
+  auto n_last = [](int p) { return 2 * p + 2 < CT ? 2 : 0; };  // last-block products into cur in phase p
+  // readout halves whose MFMAs run in phase p (even steps)
+  auto ro_halves = [](int p) { return KB == 2 ? (p == 1 ? 2 : 0) : (p == 1 || p == 3 ? 1 : 0); };
+  auto n_mfma = [&](int p, bool even) {
+    return n_last(p) * NPU + (p == 0 ? CT : CT * NPU) + (even ? ro_halves(p) * NRH : 0);
+  };
+  auto mfma_unit = [&](int p, int j, f4 (&cur)[CT], f4 (&nxt)[CT], const R1& r1, const RO& roA, const RO& roB,
+                       const bf16x8& bq) {
+    if (j < n_last(p) * NPU) {
+      const int c = 2 * p + 2 + j / NPU;
+      if (j % NPU == 0) cur[c] = mfma(Wf[c][KB - 1], Bf[KB - 1], cur[c]);
+      else if constexpr (SPLIT) cur[c] = mfma(Wf[c][KB - 1], Bl[KB - 1], cur[c]);
+      return;
+    }
+    j -= n_last(p) * NPU;
+    if (p == 0) {
+      if (j < CT) {
+        rank1_tile(r1, j, nxt);
+        return;
+      }
+      j -= CT;
+    } else {
+      if (j < CT * NPU) {
+        const int c = j / NPU, b = p - 1;
+        if (j % NPU == 0) nxt[c] = mfma(Wf[c][b], Bf[b], nxt[c]);
+        else if constexpr (SPLIT) nxt[c] = mfma(Wf[c][b], Bl[b], nxt[c]);
+        return;
+      }
+      j -= CT * NPU;
+    }
+    // readout: half A (tiles 0 .. CT/2 - 1) first, then half B
+    const int half = (KB == 2) ? j / NRH : (p == 3 ? 1 : 0);
+    readout_mma(half == 0 ? roA : roB, bq, half, j % NRH);
   };
 
   // Step s of chunk c (C, Cn, Cp: the stage buffers of chunks c, c + 1, c - 1).
   // On entry `cur` holds c (G_{t-1} W + k_t v_t^T) except the last operand
-  // block's share for tiles 2.., which phase 0 adds. The next step's
-  // accumulators `nxt` start from its rank-1 write and take operand block b
-  // right after the epilogue has produced it; block KB-1 is finished for tiles
-  // 0, 1 here and for the other tiles in the next step's phase 0.
+  // block's share for tiles 2.., which the phases add ahead of their epilogue.
+  // The next step's accumulators `nxt` start from its rank-1 write and take
+  // operand block b in phase b + 1; block KB-1 is finished for tiles 0, 1 at the
+  // step's end and for the other tiles in the next step. Each matrix instruction
+  // is followed by one state element of the epilogue, and every such group is
+  // fenced so the compiler keeps the order: a wave issues in order, and an MFMA
+  // takes the SIMD's issue port for about half of its 16 cycles, so back-to-back
+  // MFMAs leave the vector ALU idle while spread ones hide under the epilogue.
   auto step = [&](const int s, f4 (&cur)[CT], f4 (&nxt)[CT], Pre& pre, const Buf& C, const Buf& Cn,
                   const Buf& Cp, const int c) {
-    const float fg = pre.fs[0], av = pre.fs[1], m2a = pre.fs[2];
-    unsigned short* hdst = hb_w + (s & (NHS - 1)) * 16 * HROW + n * HROW + 8 * g;
-    // phase 0
-    products(KB - 1, 2, CT, cur);
-    if constexpr (SPLIT)  // no registers to spare for the early fetch
-      rank1_init(s + 1 < kChunk ? rank1_load(C, s + 1) : rank1_load(Cn, s + 1 - kChunk), nxt);
-    else
-      rank1_init(pre.r1, nxt);
-    pre.fs = *reinterpret_cast<const f4*>(s + 1 < kChunk ? C.fs + (s + 1) * 4 : Cn.fs + (s + 1 - kChunk) * 4);
-    if constexpr (!SPLIT) pre.r1 = s + 2 < kChunk ? rank1_load(C, s + 2) : rank1_load(Cn, s + 2 - kChunk);
-    epilogue(0, cur, fg, av, m2a, hdst, c * kChunk + s);
-    interleave_mfma<(SPLIT ? 2 : 1) * (CT - 2) + CT, SPLIT ? kNvPhase0Split : kNvPhase0>();
+    const float fg = pre.fs.x, av = pre.fs.y, m2a = -2.0f * av;
+    const int t = c * kChunk + s;
+    const bool even = s % 2 == 0;
+    const R1 r1 = pre.r1;
+    // the previous pair's readout operands (even steps): q and the first half
+    const Buf& RB = s >= 2 ? C : Cp;
+    const int rs0 = s >= 2 ? s - 2 : kChunk - 2, rnv = (s >= 2 || c > 0) ? 2 : 0;
+    bf16x8 bq{};
+    RO roA{}, roB{};
+    if (even) {
+      bq = readout_q(RB, rs0, rnv);
+      roA = readout_load(rs0, 0);
+      if (KB == 2) roB = readout_load(rs0, 1);
+    }
+    pre.fs = *reinterpret_cast<const float2*>(s + 1 < kChunk ? C.fs + (s + 1) * 4 : Cn.fs + (s + 1 - kChunk) * 4);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 1; b < KB; ++b) {
-      products(b - 1, 0, CT, nxt);
-      if (b == 1 && s % 2 == 0) {
-        // the previous two steps; at a chunk start they close the previous chunk
-        if (s >= 2) readout(C, s - 2, 2);
-        else readout(Cp, kChunk - 2, c > 0 ? 2 : 0);
+    for (int p = 0; p < KB; ++p) {
+      save_pre(p, cur, t);
+      if (p == 1) {  // the rank-1 operands of the step after next, once phase 0 has used this step's
+        pre.r1 = s + 2 < kChunk ? rank1_load(C, s + 2) : rank1_load(Cn, s + 2 - kChunk);
+        if (even && KB > 2) roB = readout_load(rs0, 1);
       }
-      epilogue(b, cur, fg, av, m2a, hdst, c * kChunk + s);
-      if (b == 1 && s % 2 == 0)
-        interleave_mfma<(SPLIT ? 2 : 1) * CT + CT, SPLIT ? kNvReadoutSplit : kNvReadout>();
-      else
-        interleave_mfma<(SPLIT ? 2 : 1) * CT, SPLIT ? kNvPhaseSplit : kNvPhase>();
-      __builtin_amdgcn_sched_barrier(0);
+      const int nm = n_mfma(p, even);
+      // nine VALU groups over the eight elements of tiles 2p, 2p + 1 (group q:
+      // element q's reciprocal, element q - 1's blend) and the operand block
+      float rq = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 9; ++q) {
+#pragma unroll
+        for (int j = (q * nm + 8) / 9; j < ((q + 1) * nm + 8) / 9; ++j) mfma_unit(p, j, cur, nxt, r1, roA, roB, bq);
+        const float rn = q < 8 ? elem_r(cur, 2 * p + q / 4, q % 4) : 0.0f;
+        if (q > 0) elem_g(2 * p + (q - 1) / 4, (q - 1) % 4, rq, fg, av, m2a);
+        if (q == 8) block_out(p, t);
+        rq = rn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    products(KB - 1, 0, 2, nxt);
+    // tail: the last block into tiles 0, 1 of the next step; the state tiles out
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) prod(KB - 1, cc, nxt);
+    tiles_out(s);
+    __builtin_amdgcn_sched_barrier(0);
     if (c > 0) chunk_end_work(s, c);
   };
 
   // prologue: c (H_0 W + k_0 v_0^T) for step 0, last operand block for tiles 0, 1 only
   f4 accA[CT], accB[CT];
-  rank1_init(rank1_load(buf(0), 0), accA);
+  {
+    const R1 r0 = rank1_load(buf(0), 0);
 #pragma unroll
-  for (int b = 0; b < KB - 1; ++b) products(b, 0, CT, accA);
-  products(KB - 1, 0, 2, accA);
+    for (int cc = 0; cc < CT; ++cc) rank1_tile(r0, cc, accA);
+  }
+#pragma unroll
+  for (int b = 0; b < KB - 1; ++b)
+#pragma unroll
+    for (int cc = 0; cc < CT; ++cc) prod(b, cc, accA);
+  prod(KB - 1, 0, accA);
+  prod(KB - 1, 1, accA);
   Pre pre;
-  pre.fs = *reinterpret_cast<const f4*>(buf(0).fs);
-  if constexpr (!SPLIT) pre.r1 = rank1_load(buf(0), 1);
+  pre.fs = *reinterpret_cast<const float2*>(buf(0).fs);
+  pre.r1 = rank1_load(buf(0), 1);
 
   // Chunks of 16 steps in pairs; the last chunk stops after the pair that holds
   // the sequence's last step (the pair's second step may be an identity step).
@@ -605,15 +698,22 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   if (nchunks > 0) {
     const int c = nchunks - 1;
     const int ns = Tb - c * kChunk;
+    const int ran = (ns + 1) & ~1;  // steps the loop ran in the last chunk
     if (c > 0) {
       // the previous chunk's y groups a short last chunk did not reach, before
       // the partials are overwritten
-      const int done = min(max(((ns + 1) & ~1) - 2, 0), kGroups);
+      const int done = min(max(ran - kSum0, 0), kGroups);
       for (int i = done; i < kGroups; ++i) ysum_group((c - 1) * kChunk, tid + i * L::THREADS);
       lds_barrier();
     }
-    const int te = (ns - 1) & ~1;
-    readout(buf(c % NSB), te, min(ns - te, 2));
+    const int te = ran - 2;  // the last pair: steps te, te + 1
+    const bf16x8 bq = readout_q(buf(c % NSB), te, min(ns - te, 2));
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const RO rl = readout_load(te, half);
+#pragma unroll
+      for (int j = 0; j < NRH; ++j) readout_mma(rl, bq, half, j);
+    }
     publish();
     const int t0 = c * kChunk;
     for (int grp = tid; grp < ns * (V / 4); grp += L::THREADS) ysum_group(t0, grp);
@@ -666,9 +766,9 @@ int pick_nw(int K) {
   return 0;
 }
 
-template <int V>
+template <int V, bool SPLIT>
 int lds_bytes(int nw) {
-  return nw == 4 ? Layout<V, 4>::TOTAL : Layout<V, 2>::TOTAL;
+  return nw == 4 ? Layout<V, 4, SPLIT>::TOTAL : Layout<V, 2, SPLIT>::TOTAL;
 }
 
 }  // namespace
@@ -693,12 +793,12 @@ bool mfma_supports(int K, int V, int bf16) {
 }
 
 Plan plan_mfma(int B, int H, int K, int V, bool split) {
-  (void)split;
   const int nw = pick_nw(K);
   if (!nw || (V != 64 && V != 128)) return Plan{-1, 0, 0, 0, 0, 0};
   const int R = 16 * nw, splits = K / R;
   const long long grid = (long long)B * H * splits;
-  const int lds = V == 128 ? lds_bytes<128>(nw) : lds_bytes<64>(nw);
+  const int lds = V == 128 ? (split ? lds_bytes<128, true>(nw) : lds_bytes<128, false>(nw))
+                           : (split ? lds_bytes<64, true>(nw) : lds_bytes<64, false>(nw));
   return Plan{grid > 0x7fffffffLL ? -1 : (int)grid, 64 * nw, R, splits, splits > 1 ? 1 : 0, lds};
 }
 
