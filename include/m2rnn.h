@@ -76,9 +76,15 @@ typedef enum m2rnn_dtype {
  *             (round-to-nearest-even) as the matrix operand and fp32
  *             accumulation; rank-1 write, tanh, gate blend and readout are
  *             fused in the same kernel. Fastest; per-step operand rounding of
- *             2^-9 relative, which a sensitive trajectory can amplify.
+ *             2^-9 relative, which a sensitive trajectory can amplify: on the
+ *             workloads with gates near 1 and inputs scaled by 1/sqrt(K)
+ *             (B=4 H=8 K=V=64 T=512, and B=2 H=16 K=64 V=128 T=32768) it misses
+ *             the 2e-2 normwise bar (measured on all units: H_T 2.2e-2 on the
+ *             first, y 2.4e-2 on the second); on the others it is ~2e-3.
  * MFMA_SPLIT: as MFMA with the state operand split into bf16 hi + bf16 lo and
- *             two MFMA passes (~2^-17 relative operand error).
+ *             two MFMA passes (~2^-17 relative operand error); the readout
+ *             takes both halves too (y and H_T within ~1e-5 to 3e-4 of the
+ *             fp64 definition on every workload measured).
  * AUTO:       bf16 with V in {64, 128}, T > 1 and at most 768 16-row tiles
  *             (B H K / 16 <= 768; two workgroups fit per CU of a 256-CU
  *             gfx950): MFMA_LONG_SPLIT; else MFMA_SPLIT where it covers the
@@ -93,7 +99,10 @@ typedef enum m2rnn_dtype {
  *             adds whose order, and hence y's last bits, can vary between runs
  *             (H_T cannot). bf16, K in {16, ..., 128}, V in {64, 128}; the
  *             training forwards take them for K in {32, 64, 128} (the shapes
- *             the backward pass covers) and write the same `saved` layout. */
+ *             the backward pass covers) and write the same `saved` layout.
+ *             MFMA_LONG has MFMA's precision (misses the bar on the same two
+ *             workloads: H_T 2.6e-2, y 2.6e-2); MFMA_LONG_SPLIT has MFMA_SPLIT's
+ *             state precision. */
 typedef enum m2rnn_algo {
   M2RNN_ALGO_AUTO = 0,
   M2RNN_ALGO_SIMPLE = 1,
