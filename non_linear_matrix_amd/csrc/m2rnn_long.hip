@@ -316,9 +316,12 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
     const unsigned int* kx = kx_all + sb * kChunk * 16;
     const unsigned int* vx = vx_all + sb * kChunk * 16 * L::NVX;
     const unsigned int kp = *((g == 0) ? kx + s * 16 + n : zero_lds);
-    const u4 win = *reinterpret_cast<const u4*>(vx + (s * 16 + n) * L::NVX + 4 * w);
-    acc[0] = mfma(__builtin_bit_cast(bf16x8, win), __builtin_bit_cast(bf16x8, u4{kp, 0u, 0u, 0u}), f4{0, 0, 0, 0});
-    acc[1] = mfma(__builtin_bit_cast(bf16x8, win), __builtin_bit_cast(bf16x8, u4{0u, kp, 0u, 0u}), f4{0, 0, 0, 0});
+    // 16x16x16: A the (v, v) pairs of tiles 2w, 2w + 1, B the (hi, lo) pair of c k
+    // in the slots of the tile (the record's two zero dwords are not read)
+    const uint2 win = *reinterpret_cast<const uint2*>(vx + (s * 16 + n) * L::NVX + 4 * w);
+    const s4 av4 = __builtin_bit_cast(s4, win);
+    acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av4, __builtin_bit_cast(s4, uint2{kp, 0u}), f4{0, 0, 0, 0}, 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av4, __builtin_bit_cast(s4, uint2{0u, kp}), f4{0, 0, 0, 0}, 0, 0, 0);
   };
   auto products = [&](int o, f4 (&acc)[2]) {
 #pragma unroll
@@ -333,8 +336,10 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
   f4 Dr[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
   // in two parts, so that the LDS reads go out with the exchange's and the
   // MFMAs follow the step's products
+  // with SPLIT the low halves of the state are read out too (their tiles are
+  // exchanged anyway), so y carries the split operand's precision
   struct ReadoutOps {
-    bf16x8 q, s[2];
+    bf16x8 q, s[2], sl[SPLIT ? 2 : 1];
   };
   auto readout_load = [&](int sb, int s0, int nvalid) {
     ReadoutOps r;
@@ -350,12 +355,22 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
       const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s4*)(src + 16 * P + 4 * HROW));
       r.s[j] = __builtin_bit_cast(bf16x8, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      if constexpr (SPLIT) {
+        const unsigned short* srl = xl + (s & 1) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
+        const s4 llo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(srl + 16 * P));
+        const s4 lhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(srl + 16 * P + 4 * HROW));
+        r.sl[j] = __builtin_bit_cast(bf16x8, s8{llo[0], llo[1], llo[2], llo[3], lhi[0], lhi[1], lhi[2], lhi[3]});
+      }
     }
     return r;
   };
   auto readout_mma = [&](const ReadoutOps& r) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) Dr[j] = mfma(r.s[j], r.q, Dr[j]);
+    for (int j = 0; j < 2; ++j) {
+      Dr[j] = mfma(r.s[j], r.q, Dr[j]);
+      if constexpr (SPLIT) Dr[j] = mfma(r.sl[j], r.q, Dr[j]);
+    }
   };
   // this wave's columns of y for the steps t0 .. t0 + nsteps - 1, added into y.
   // A chunk's sums are added at step 1 of the next chunk, after that step's
@@ -373,11 +388,18 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
 #pragma unroll
         for (int i = 0; i < 4; ++i) ys[n * L::YS_ROW + 16 * (g % 2) + 8 * j + 4 * (g / 2) + i] = Dp[j][i] * kInvC;
       __builtin_amdgcn_wave_barrier();
+      // every value first, then the adds with no branch between them: a row
+      // past the sequence's end adds zero to the chunk's last valid row (x + 0
+      // is x), so the adds need no predicate and the reads one wait
+      float val[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) val[r] = ys[(2 * r + l / 32) * L::YS_ROW + l % 32];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int row = 2 * r + l / 32;
-        const float val = ys[row * L::YS_ROW + l % 32];
-        if (row < pend_n) unsafeAtomicAdd(a.y + (unit * LD + pend_t0 + row) * V + 32 * w + l % 32, val);
+        const bool live = row < pend_n;
+        unsafeAtomicAdd(a.y + (unit * LD + pend_t0 + (live ? row : pend_n - 1)) * V + 32 * w + l % 32,
+                        live ? val[r] : 0.0f);
       }
     }
     pend_n = 0;
