@@ -69,7 +69,13 @@ typedef enum m2rnn_dtype {
 
 /* Kernel family.
  * SIMPLE:     one workgroup per (b, h), fp32 arithmetic from LDS; covers every
- *             supported shape and both dtypes (the fp32 path).
+ *             supported shape and both dtypes.
+ * MFMA_F32:   fp32 inputs, every supported K and V: the fp32 path on the matrix
+ *             cores. One workgroup of K/16 waves per (b, h); the state, W, the
+ *             rank-1 term and the readout stay fp32 (H_{t-1} W on
+ *             v_mfma_f32_16x16x4_f32, no operand rounding beyond fp32). y is
+ *             summed over the waves in a fixed order and written once, so every
+ *             output is bitwise repeatable.
  * MFMA:       bf16 inputs, K in {32, 64, 128}, V in {64, 128}; the fp32 state
  *             stays in registers across all steps, H_{t-1} W runs on
  *             v_mfma_f32_16x16x32_bf16 with the state rounded to bf16
@@ -85,10 +91,10 @@ typedef enum m2rnn_dtype {
  *             two MFMA passes (~2^-17 relative operand error); the readout
  *             takes both halves too (y and H_T within ~1e-5 to 3e-4 of the
  *             fp64 definition on every workload measured).
- * AUTO:       bf16 with V in {64, 128}, T > 1 and at most 768 16-row tiles
- *             (B H K / 16 <= 768; two workgroups fit per CU of a 256-CU
- *             gfx950): MFMA_LONG_SPLIT; else MFMA_SPLIT where it covers the
- *             shape, else SIMPLE. With M2RNN_FLAG_DETERMINISTIC it never takes
+ * AUTO:       fp32: MFMA_F32. bf16 with V in {64, 128}, T > 1 and at most
+ *             768 16-row tiles (B H K / 16 <= 768; two workgroups fit per CU of
+ *             a 256-CU gfx950): MFMA_LONG_SPLIT; else MFMA_SPLIT where it covers
+ *             the shape, else SIMPLE. With M2RNN_FLAG_DETERMINISTIC it never takes
  *             MFMA_LONG*.
  * MFMA_LONG, MFMA_LONG_SPLIT: the same arithmetic as MFMA / MFMA_SPLIT, for
  *             workloads with few 16-row tiles (B H K / 16 well below the GPU's
@@ -102,14 +108,15 @@ typedef enum m2rnn_dtype {
  *             the backward pass covers) and write the same `saved` layout.
  *             MFMA_LONG has MFMA's precision (misses the bar on the same two
  *             workloads: H_T 2.6e-2, y 2.6e-2); MFMA_LONG_SPLIT has MFMA_SPLIT's
- *             state precision. */
+ *             (both halves in the products and the readout). */
 typedef enum m2rnn_algo {
   M2RNN_ALGO_AUTO = 0,
   M2RNN_ALGO_SIMPLE = 1,
   M2RNN_ALGO_MFMA = 2,
   M2RNN_ALGO_MFMA_SPLIT = 3,
   M2RNN_ALGO_MFMA_LONG = 4,
-  M2RNN_ALGO_MFMA_LONG_SPLIT = 5
+  M2RNN_ALGO_MFMA_LONG_SPLIT = 5,
+  M2RNN_ALGO_MFMA_F32 = 6
 } m2rnn_algo;
 
 /* The forward recurrence with the automatically chosen kernel. */
@@ -353,7 +360,7 @@ const char* m2rnn_status_string(m2rnn_status status);
  * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones and the front-end, 0.4.0 MFMA_LONG, 0.5.0 AUTO's
  * choice of MFMA_LONG_SPLIT and M2RNN_FLAG_DETERMINISTIC, 0.6.0 MFMA_LONG* in
  * the training forwards and m2rnn_bwd_algo, 0.7.0 m2rnn_get_plan_ex and
- * m2rnn_bwd_noalloc). */
+ * m2rnn_bwd_noalloc, 0.8.0 MFMA_F32). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libm2rnn.so")
 OBJDIR = os.path.join(ROOT, "_build")
 SOURCES = ["m2rnn_api.cpp", "m2rnn_simple.hip", "m2rnn_mfma.hip", "m2rnn_bwd.hip", "m2rnn_ckpt.cpp",
-           "m2rnn_frontend.hip", "m2rnn_decode.hip", "m2rnn_long.hip", "m2rnn_bwd_long.hip", "m2rnn_noalloc.hip"]
+           "m2rnn_frontend.hip", "m2rnn_decode.hip", "m2rnn_long.hip", "m2rnn_bwd_long.hip", "m2rnn_noalloc.hip",
+           "m2rnn_f32.hip"]
 ARCH = "gfx950"
 
 

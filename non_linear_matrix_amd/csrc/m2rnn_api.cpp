@@ -44,6 +44,8 @@ m2rnn_status check(const void* k, const void* v, const void* q, const void* f, c
     case M2RNN_ALGO_MFMA_LONG:
     case M2RNN_ALGO_MFMA_LONG_SPLIT:
       return (dt == M2RNN_DTYPE_BF16 && (V == 64 || V == 128)) ? M2RNN_SUCCESS : M2RNN_ERROR_NOT_SUPPORTED;
+    case M2RNN_ALGO_MFMA_F32:
+      return (dt == M2RNN_DTYPE_F32 && m2rnn::mfma_f32_supports(K, V)) ? M2RNN_SUCCESS : M2RNN_ERROR_NOT_SUPPORTED;
     default:
       return M2RNN_ERROR_NOT_SUPPORTED;
   }
@@ -132,6 +134,7 @@ m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dty
   // multi-step kernel (one wave per tile, 1024 at once); beyond that the latter
   // wins (measured at K = V = 128).
   constexpr long double kLongMaxTiles = 768;
+  if (in_dtype == M2RNN_DTYPE_F32 && m2rnn::mfma_f32_supports(K, V)) return M2RNN_ALGO_MFMA_F32;
   if (in_dtype == M2RNN_DTYPE_BF16 && T > 1 && (V == 64 || V == 128) && supported_dim(K) &&
       (long double)B * H * (K / 16) <= kLongMaxTiles)
     return M2RNN_ALGO_MFMA_LONG_SPLIT;
@@ -156,6 +159,8 @@ m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const
   else if (algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT)
     e = m2rnn::decode_supports(a) ? m2rnn::launch_decode(a, s)  // one step: the decoding kernel
                                   : m2rnn::launch_long(a, algo == M2RNN_ALGO_MFMA_LONG_SPLIT, s);
+  else if (algo == M2RNN_ALGO_MFMA_F32)
+    e = m2rnn::launch_mfma_f32(a, s);
   else
     e = m2rnn::launch_simple(a, s);
   return e == hipSuccess ? M2RNN_SUCCESS : M2RNN_ERROR_LAUNCH;
@@ -363,7 +368,8 @@ m2rnn_status m2rnn_get_plan_ex(int B, int H, int T, int K, int V, m2rnn_dtype in
   if ((st = resolve_algo(algo, B, H, T, K, V, in_dtype, flags)) != M2RNN_SUCCESS) return st;
   const bool mf = algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT;
   const bool lg = algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT;
-  m2rnn::Plan pl = !(mf || lg) ? m2rnn::plan_simple(B, H, K, V)
+  m2rnn::Plan pl = algo == M2RNN_ALGO_MFMA_F32 ? m2rnn::plan_mfma_f32(B, H, K, V)
+                   : !(mf || lg)                 ? m2rnn::plan_simple(B, H, K, V)
                    : T == 1 && m2rnn::mfma_supports(K, V, 1) ? m2rnn::plan_decode(B, H, K, V)
                    : lg ? m2rnn::plan_long(B, H, K, V)
                         : m2rnn::plan_mfma(B, H, K, V, algo == M2RNN_ALGO_MFMA_SPLIT);
@@ -402,6 +408,6 @@ const char* m2rnn_status_string(m2rnn_status status) {
   }
 }
 
-int m2rnn_version(void) { return 700; }
+int m2rnn_version(void) { return 800; }
 
 }  // extern "C"

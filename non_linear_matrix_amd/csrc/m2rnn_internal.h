@@ -52,6 +52,10 @@ hipError_t launch_simple(const FwdArgs& a, hipStream_t stream);
 // split: state operand as bf16 hi + lo (two MFMA passes) instead of one bf16.
 hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream);
 bool mfma_supports(int K, int V, int bf16);
+// fp32 matrix-core kernel (m2rnn_f32.hip): fp32 inputs, no saved data; writes y
+// itself in a fixed summation order (clears it only for ragged lengths).
+bool mfma_f32_supports(int K, int V);
+hipError_t launch_mfma_f32(const FwdArgs& a, hipStream_t stream);
 // workgroups the multi-step kernel gives one (b, h) unit (0: K not covered)
 int mfma_groups(int K);
 // One-step kernel (m2rnn_decode.hip): T == 1, no saved data, bf16, MFMA shapes.
@@ -116,6 +120,7 @@ struct Plan {
 Plan plan_simple(int B, int H, int K, int V);
 Plan plan_mfma(int B, int H, int K, int V, bool split);
 Plan plan_decode(int B, int H, int K, int V);
+Plan plan_mfma_f32(int B, int H, int K, int V);
 // Latency-oriented forward (m2rnn_long.hip): one workgroup of V/32 waves per
 // 16-row tile; y summed over the tiles with atomic adds.
 bool long_supports(const FwdArgs& a);

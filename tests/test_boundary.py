@@ -28,7 +28,7 @@ def _check(**over):
 def test_library_exists_and_loads():
     assert os.path.exists(m2rnn.LIB_PATH), "build the library first (python -m non_linear_matrix_amd.build)"
     lib = m2rnn.load()
-    assert m2rnn.version() == 700
+    assert m2rnn.version() == 800
 
 
 def test_every_declared_symbol_is_exported():
@@ -92,13 +92,28 @@ def test_unknown_dtype_and_algo():
 
 @pytest.mark.parametrize("algo", ["mfma", "mfma_split"])
 def test_mfma_coverage(algo):
-    assert _check(dtype="f32", algo=algo) == UNSUPPORTED          # fp32 inputs: simple kernel only
+    assert _check(dtype="f32", algo=algo) == UNSUPPORTED          # fp32 inputs: the fp32 kernels
     assert _check(K=16, V=128, algo=algo) == UNSUPPORTED          # fewer than 32 rows
     assert _check(K=96, V=128, algo=algo) == UNSUPPORTED          # more than two row groups
     assert _check(K=128, V=96, algo=algo) == UNSUPPORTED
     for K in (32, 64, 128):
         for V in (64, 128):
             assert _check(K=K, V=V, algo=algo) == OK
+
+
+def test_mfma_f32_coverage():
+    """The fp32 matrix-core family takes fp32 inputs of every supported shape and
+    nothing else; it has one fixed y summation order, so AUTO keeps it under
+    M2RNN_FLAG_DETERMINISTIC, with or without accumulation."""
+    for K in range(16, 129, 16):
+        for V in range(16, 129, 16):
+            assert _check(dtype="f32", K=K, V=V, algo="mfma_f32") == OK, (K, V)
+    assert _check(K=64, V=64, algo="mfma_f32") == UNSUPPORTED     # bf16 inputs
+    assert _check(dtype="f32", K=20, V=64, algo="mfma_f32") == UNSUPPORTED
+    det, acc = m2rnn.FLAG_DETERMINISTIC, m2rnn.FLAG_ACCUMULATE_Y
+    for flags in (det, det | acc):
+        assert m2rnn.get_plan(8, 16, 64, 128, 128, "f32", "auto", flags)["algo"] == "mfma_f32"
+    assert m2rnn.get_plan(8, 16, 64, 128, 128, "f32", "mfma_f32", det | acc)["algo"] == "mfma_f32"
 
 
 def test_launch_plans():
@@ -109,7 +124,14 @@ def test_launch_plans():
     p = m2rnn.get_plan(2, 16, 32768, 64, 128, "bf16", "mfma")
     assert p["grid"] == 32 and p["groups_per_unit"] == 1 and p["clears_y"] == 0
     p = m2rnn.get_plan(1, 1, 64, 16, 16, "f32", "auto")
-    assert p["algo"] == "simple" and p["grid"] == 1
+    assert p["algo"] == "mfma_f32" and p["grid"] == 1 and p["block"] == 64 and p["clears_y"] == 0
+    # fp32 on the matrix cores: one workgroup of K/16 waves per unit, LDS within a CU's 160 KiB
+    for K in range(16, 129, 16):
+        for V in range(16, 129, 16):
+            p = m2rnn.get_plan(3, 5, 100, K, V, "f32", "mfma_f32")
+            assert p["grid"] == 15 and p["block"] == 4 * K and p["groups_per_unit"] == 1, (K, V)
+            assert 0 < p["lds_bytes"] <= 160 * 1024, (K, V)
+    assert m2rnn.get_plan(1, 1, 64, 16, 16, "f32", "simple")["algo"] == "simple"
     # the latency-oriented kernel: one workgroup of V/32 waves per 16-row tile
     p = m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "mfma_long")
     assert p["grid"] == 32 * 8 and p["block"] == 256 and p["clears_y"] == 1
@@ -129,7 +151,7 @@ def test_unknown_flag_bits_are_rejected():
 
 def test_auto_picks_a_kernel_that_covers_the_shape():
     assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "bf16") == "mfma_split"     # 1024 row tiles
-    assert m2rnn.pick_algo(1, 1, 64, 16, 16, "f32") == "simple"
+    assert m2rnn.pick_algo(1, 1, 64, 16, 16, "f32") == "mfma_f32"
     assert m2rnn.pick_algo(1, 1, 64, 16, 96, "bf16") == "simple"
     # up to 768 16-row tiles: the latency-oriented kernel
     assert m2rnn.pick_algo(1, 1, 64, 16, 128, "bf16") == "mfma_long_split"
@@ -139,7 +161,8 @@ def test_auto_picks_a_kernel_that_covers_the_shape():
     assert m2rnn.pick_algo(6, 16, 100, 128, 128, "bf16") == "mfma_long_split"  # 768 tiles
     assert m2rnn.pick_algo(7, 16, 100, 128, 128, "bf16") == "mfma_split"       # 896 tiles
     assert m2rnn.pick_algo(1, 32, 1, 128, 128, "bf16") == "mfma_split"         # one step: decoding kernel
-    assert m2rnn.pick_algo(1, 4, 64, 32, 64, "f32") == "simple"
+    assert m2rnn.pick_algo(1, 4, 64, 32, 64, "f32") == "mfma_f32"
+    assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "f32") == "mfma_f32"
     p = m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "auto")
     assert p["algo"] == "mfma_long_split" and p["grid"] == 256 and p["block"] == 256 and p["clears_y"] == 1
 
@@ -307,7 +330,7 @@ def test_training_forwards_take_the_long_kernel_only_where_the_backward_covers_t
                                                           2, 2, 16, K, V, bf16, alg, None)
         assert bw(16, 64) == UNSUPPORTED, algo
         assert bw(64, 64, dk=None) == INVALID, algo
-    for other in ("simple", 6, 99):
+    for other in ("simple", "mfma_f32", 99):
         alg = m2rnn.ALGOS[other] if isinstance(other, str) else other
         assert lib.m2rnn_bwd_algo(p, p, p, p, p, None, p, p, None, p, p, p, p, p, None, p, 2, 2, 16, 64, 64, bf16,
                                   alg, None) == UNSUPPORTED, other
