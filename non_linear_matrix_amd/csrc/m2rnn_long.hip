@@ -316,12 +316,16 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
     const unsigned int* kx = kx_all + sb * kChunk * 16;
     const unsigned int* vx = vx_all + sb * kChunk * 16 * L::NVX;
     const unsigned int kp = *((g == 0) ? kx + s * 16 + n : zero_lds);
-    // 16x16x16: A the (v, v) pairs of tiles 2w, 2w + 1, B the (hi, lo) pair of c k
-    // in the slots of the tile (the record's two zero dwords are not read)
-    const uint2 win = *reinterpret_cast<const uint2*>(vx + (s * 16 + n) * L::NVX + 4 * w);
-    const s4 av4 = __builtin_bit_cast(s4, win);
-    acc[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av4, __builtin_bit_cast(s4, uint2{kp, 0u}), f4{0, 0, 0, 0}, 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av4, __builtin_bit_cast(s4, uint2{0u, kp}), f4{0, 0, 0, 0}, 0, 0, 0);
+    // 16x16x32: A the record (v pairs of tiles 2w, 2w + 1, then its two zero
+    // dwords), B the (hi, lo) pair of c k in the slots of the tile. Not the
+    // 16x16x16 form: on gfx950 a 16x16x32 product that took a 16x16x16 result as
+    // its accumulator a few instructions later read it before the result was
+    // there, and here the compiler places the rank-1 write within a few
+    // instructions of the first product into the same accumulator.
+    const u4 win = *reinterpret_cast<const u4*>(vx + (s * 16 + n) * L::NVX + 4 * w);
+    const bf16x8 av = __builtin_bit_cast(bf16x8, win);
+    acc[0] = mfma(av, __builtin_bit_cast(bf16x8, u4{kp, 0u, 0u, 0u}), f4{0, 0, 0, 0});
+    acc[1] = mfma(av, __builtin_bit_cast(bf16x8, u4{0u, kp, 0u, 0u}), f4{0, 0, 0, 0});
   };
   auto products = [&](int o, f4 (&acc)[2]) {
 #pragma unroll

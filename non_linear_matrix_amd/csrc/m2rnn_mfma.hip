@@ -88,17 +88,23 @@ struct Layout {
   static constexpr int CT = V / 16;   // 16-column tiles
   static constexpr int KB = V / 32;   // 32-wide contraction blocks
   // dwords per row and step of the rank-1 A operands: per tile pair k, dwords
-  // 4k .. 4k+3 = (v pair of tile 2k, v pair of tile 2k+1, 0, 0), so one aligned
-  // 16-byte read is the operand; the 4 padding dwords make those reads
-  // conflict-free across a row group
-  static constexpr int NVX = 2 * CT + 4;
+  // 2k, 2k+1 = (v pair of tile 2k, v pair of tile 2k+1), one aligned 8-byte read;
+  // the 2 padding dwords put the 16 rows a 16-lane group reads on distinct banks
+  static constexpr int NVX = CT + 2;
   static constexpr int HROW = V + 8;  // bf16 per LDS state row (padded)
   // floats per row of the partial readouts: the 4-float pad puts the 16 rows a
   // publishing 16-lane group writes on distinct banks (unpadded, all 16 hit the same)
   static constexpr int YROW = V + 4;
-  // stage buffers: chunk c+1 goes into chunk c-1's buffer early in chunk c, once
-  // the readout of chunk c-1's last steps (step 0 of chunk c) is behind a barrier
-  static constexpr int NSB = 2;
+  // One LDS barrier per chunk where three stage buffers and two partial-readout
+  // buffers fit (the single operand): chunk c+2 is staged early in chunk c into
+  // chunk c-1's buffer and becomes visible at the next chunk's barrier, and the
+  // partials alternate between buffers. Otherwise (the split operand, whose
+  // state tiles take twice the room) two buffers of each and a second barrier
+  // per chunk: chunk c+1 is staged early in chunk c and made visible mid-chunk,
+  // and the partials are summed before that barrier.
+  static constexpr bool ONEBAR = !SPLIT;
+  static constexpr int NSB = ONEBAR ? 3 : 2;
+  static constexpr int NYP = ONEBAR ? 2 : 1;
   // state-tile slots per wave: a step pair's readout operands are read at the
   // start of the next pair, before its first step overwrites the older slot
   static constexpr int NHS = 2;
@@ -110,7 +116,7 @@ struct Layout {
   static constexpr int QS_BYTES = NSB * kChunk * R * 2;          // q, bf16
   static constexpr int FS_BYTES = NSB * kChunk * 4 * 4;          // f, a, -2a, pad
   static constexpr int HB_BYTES = NW * NHS * NPL * 16 * HROW * 2;  // per-wave state tiles
-  static constexpr int YP_BYTES = NW * kChunk * YROW * 4;        // per-wave partial readouts
+  static constexpr int YP_BYTES = NYP * NW * kChunk * YROW * 4;  // per-wave partial readouts
   static constexpr int Z_BYTES = 16;                             // zeros
   static constexpr int KX_OFF = 0;
   static constexpr int VX_OFF = KX_OFF + KX_BYTES;
@@ -211,7 +217,7 @@ struct Stager {
           const int col = 8 * part + i;
           const unsigned int raw = (r[i / 2] >> (16 * (i % 2))) & 0xffffu;
           const int tile = col / 16;
-          vx[(s * 16 + col % 16) * L::NVX + 4 * (tile / 2) + tile % 2] = raw | (raw << 16);
+          vx[(s * 16 + col % 16) * L::NVX + 2 * (tile / 2) + tile % 2] = raw | (raw << 16);
         }
       }
     }
@@ -340,11 +346,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     lds_barrier();  // every wave has its fragments before the region is cleared
   }
 
-  // ---- one-time LDS init: the zero dwords of the rank-1 operands, the state tiles,
-  // the zero word; then chunks 0 and 1 into the stage buffers (other addresses)
-  for (int i = tid; i < NSB * kChunk * 16; i += L::THREADS)
-#pragma unroll
-    for (int k = 0; k < CT / 2; ++k) *reinterpret_cast<uint2*>(vx_all + i * NVX + 4 * k + 2) = uint2{0u, 0u};
+  // ---- one-time LDS init: the state tiles, the zero word; then chunks 0 and 1
+  // into the stage buffers (other addresses)
   for (int i = tid; i < L::HB_BYTES / 4; i += L::THREADS)
     reinterpret_cast<unsigned int*>(lds + L::HB_OFF)[i] = 0u;
   if (tid < 4) reinterpret_cast<unsigned int*>(lds + L::Z_OFF)[tid] = 0u;
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     r.kpair = *kp;
     const unsigned int* vp = B.vx + (s * 16 + n) * NVX;
 #pragma unroll
-    for (int k = 0; k < CT / 2; ++k) r.win[k] = *reinterpret_cast<const uint2*>(vp + 4 * k);
+    for (int k = 0; k < CT / 2; ++k) r.win[k] = *reinterpret_cast<const uint2*>(vp + 2 * k);
     return r;
   };
 
@@ -447,12 +450,14 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   float* y = a.y;
   const bool atomic_y = splits > 1 || a.accumulate;
 
-  // y for the steps t0 .. t0 + nsteps - 1 of one chunk from the summed partials
-  auto ysum_group = [&](int t0, int grp) {
+  // y of one group (a step and 4 positions) of the chunk starting at t0, from the
+  // waves' partials in partial buffer yb, added in wave order
+  auto ysum_group = [&](int t0, int grp, int yb) {
+    const float* ypb = yp_all + yb * NW * kChunk * L::YROW;
     const int sn = grp / (V / 4), pos = 4 * (grp % (V / 4));
-    f4 sum = *reinterpret_cast<const f4*>(yp_all + sn * L::YROW + pos);
+    f4 sum = *reinterpret_cast<const f4*>(ypb + sn * L::YROW + pos);
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(yp_all + (ww * kChunk + sn) * L::YROW + pos);
+    for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(ypb + (ww * kChunk + sn) * L::YROW + pos);
     sum *= kInvC;
     // position 16 P + 4 gg  ->  column 32 (P/2) + 16 (gg%2) + 8 (P%2) + 4 (gg/2)
     const int P = pos / 16, gg = (pos % 16) / 4;
@@ -467,23 +472,27 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // Chunk end, spread over the first steps of the next chunk so that its LDS
-  // round trips overlap with their compute:
-  //   step 1 (end): publish the waves' partial readouts of the finished chunk
-  //                 (Dr, which the readout MFMAs of steps 0 and 1 have just
-  //                 completed with the chunk's last pair); LDS barrier
-  //   step 2:       stage the next chunk from the registers loaded a chunk ago,
-  //                 then fetch the one after it
+  // Chunk end of chunk c - 1, spread over the first steps of chunk c so that its
+  // LDS round trips overlap with their compute:
+  //   step 1 (end): publish the waves' partial readouts of chunk c - 1 (Dr,
+  //                 which the readout MFMAs of steps 0 and 1 have just completed
+  //                 with its last pair); LDS barrier
+  //   step 2:       stage a chunk from the registers loaded a chunk ago (c + 2
+  //                 with one barrier per chunk, which this step runs in chunk 0
+  //                 too; else c + 1), then fetch the one after it
   //   steps 3..:    sum the partials into y, one group per step and thread
-  //   step kSync:   LDS barrier: the staged chunk is visible before the step
-  //                 that first prefetches from it (step 14), and every wave has
-  //                 summed before the next chunk end overwrites the partials
+  //   step kSync:   (two barriers per chunk only) LDS barrier: the staged chunk
+  //                 is visible before the step that first prefetches from it
+  //                 (step 14), and every wave has summed before the next chunk
+  //                 end overwrites the partials
+  constexpr bool ONEBAR = L::ONEBAR;
   constexpr int kGroups = kChunk * (V / 4) / L::THREADS;  // y-sum groups per thread
   static_assert(kGroups * L::THREADS == kChunk * (V / 4), "whole groups per thread");
   constexpr int kSum0 = 3, kSync = 8;
   static_assert(kSum0 + kGroups <= kSync && kSync < kChunk - 2, "chunk-end schedule");
-  auto publish = [&]() {
-    float* ypw = yp_all + w * kChunk * L::YROW;
+  auto ybuf = [](int c) { return ONEBAR ? (c & 1) : 0; };  // partial buffer of chunk c
+  auto publish = [&](int yb) {
+    float* ypw = yp_all + (yb * NW + w) * kChunk * L::YROW;
 #pragma unroll
     for (int P = 0; P < CT; ++P) *reinterpret_cast<f4*>(ypw + n * L::YROW + 16 * P + 4 * g) = Dr[P];
 #pragma unroll
@@ -497,10 +506,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     }
   };
   auto chunk_end_work = [&](int s, int c) {
-    if (s == 1) publish();
-    if (s == 2) stage_next(c + 1);
-    if (s >= kSum0 && s < kSum0 + kGroups) ysum_group((c - 1) * kChunk, tid + (s - kSum0) * L::THREADS);
-    if (s == kSync) lds_barrier();
+    if (c > 0 && s == 1) publish(ybuf(c - 1));
+    if (s == 2 && (ONEBAR || c > 0)) stage_next(ONEBAR ? c + 2 : c + 1);
+    if (c > 0 && s >= kSum0 && s < kSum0 + kGroups)
+      ysum_group((c - 1) * kChunk, tid + (s - kSum0) * L::THREADS, ybuf(c - 1));
+    if (!ONEBAR && c > 0 && s == kSync) lds_barrier();
   };
 
   // one state element, tile c, register i, in two parts so that consecutive
@@ -514,21 +524,18 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   auto elem_g = [&](int c, int i, float r, float fg, float av, float m2a) {
     G[c][i] = fmaf(m2a, r, fmaf(fg, G[c][i], av));
   };
-  // the operand block b for the next product from the new tiles 2b, 2b + 1
-  auto block_out = [&](int b, int t) {
+  // the operand block b for the next product from the new tiles 2b, 2b + 1, and
+  // the block's rounded state into step s's readout slot(s). A slot is read for
+  // the readout two steps later, half A at that step's start and half B (blocks
+  // KB/2 .. KB-1) at its phase 1, before the same step writes those blocks.
+  auto block_out = [&](int b, int t, int s) {
     make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
     if constexpr (SAVE) {
       if (t < T) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, t + 1, T, a.K, V) + rt_off + b * 1024) = Bf[b];
     }
-  };
-  // the step's rounded state tiles to its readout slot(s), at the step's end
-  auto tiles_out = [&](int s) {
     unsigned short* hdst = hb_w + (s & (NHS - 1)) * NPL * 16 * HROW + n * HROW + 8 * g;
-#pragma unroll
-    for (int b = 0; b < KB; ++b) {
-      *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
-      if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(hdst + 16 * HROW + 32 * b) = Bl[b];
-    }
+    *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
+    if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(hdst + 16 * HROW + 32 * b) = Bl[b];
   };
   // training forward: the pre-activation c A_t of tiles 2b, 2b+1, as bf16
   auto save_pre = [&](int b, const f4 (&cur)[CT], int t) {
@@ -547,12 +554,29 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     acc[c] = mfma(Wf[c][b], Bf[b], acc[c]);
     if constexpr (SPLIT) acc[c] = mfma(Wf[c][b], Bl[b], acc[c]);
   };
-  // rank-1 write c k v^T of a step into tile c as the accumulator's start
-  // (16x16x16: the pair (v, v) of the tile against (hi, lo) of c k)
+  // rank-1 write c k v^T of a step into tile c as the accumulator's start: the
+  // pair (v, v) of the tile against (hi, lo) of c k.
+  //
+  // In the step loop this is a 16x16x16 product (fewer issue cycles than the
+  // 16x16x32 form). On gfx950 a 16x16x32 product that takes a 16x16x16 result as
+  // its accumulator only four instructions later, with no wait between them (as
+  // the compiler scheduled it), read the accumulator before the result was in
+  // it. In the loop the fenced phase schedule puts a whole phase (tens of
+  // instructions) between a step's rank-1 write and the first product into that
+  // accumulator; a build test checks that distance on the disassembly. The
+  // prologue, where the products follow at once, takes the 16x16x32 form (the
+  // pair in its first k slots, the others zero), whose accumulation into the
+  // next 16x16x32 product the compiler orders.
   auto rank1_tile = [&](const R1& r, int c, f4 (&acc)[CT]) {
     const s4 av4 = __builtin_bit_cast(s4, r.win[c / 2]);
-    const s4 bk = __builtin_bit_cast(s4, (c & 1) ? uint2{0u, r.kpair} : uint2{r.kpair, 0u});
-    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av4, bk, f4{0, 0, 0, 0}, 0, 0, 0);
+    const s4 bk4 = __builtin_bit_cast(s4, (c & 1) ? uint2{0u, r.kpair} : uint2{r.kpair, 0u});
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av4, bk4, f4{0, 0, 0, 0}, 0, 0, 0);
+  };
+  auto rank1_tile_prologue = [&](const R1& r, int c, f4 (&acc)[CT]) {
+    const uint2 wv = r.win[c / 2];
+    const bf16x8 av = __builtin_bit_cast(bf16x8, u4{wv.x, wv.y, 0u, 0u});
+    const bf16x8 bk = __builtin_bit_cast(bf16x8, (c & 1) ? u4{0u, r.kpair, 0u, 0u} : u4{r.kpair, 0u, 0u, 0u});
+    acc[c] = mfma(av, bk, f4{0, 0, 0, 0});
   };
 
   // per-step operands fetched ahead: the gate scalars of the next step and the
@@ -652,17 +676,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
         for (int j = (q * nm + 8) / 9; j < ((q + 1) * nm + 8) / 9; ++j) mfma_unit(p, j, cur, nxt, r1, roA, roB, bq);
         const float rn = q < 8 ? elem_r(cur, 2 * p + q / 4, q % 4) : 0.0f;
         if (q > 0) elem_g(2 * p + (q - 1) / 4, (q - 1) % 4, rq, fg, av, m2a);
-        if (q == 8) block_out(p, t);
+        if (q == 8) block_out(p, t, s);
         rq = rn;
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // tail: the last block into tiles 0, 1 of the next step; the state tiles out
+    // tail: the last block into tiles 0, 1 of the next step
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) prod(KB - 1, cc, nxt);
-    tiles_out(s);
     __builtin_amdgcn_sched_barrier(0);
-    if (c > 0) chunk_end_work(s, c);
+    chunk_end_work(s, c);
   };
 
   // prologue: c (H_0 W + k_0 v_0^T) for step 0, last operand block for tiles 0, 1 only
@@ -670,7 +693,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   {
     const R1 r0 = rank1_load(buf(0), 0);
 #pragma unroll
-    for (int cc = 0; cc < CT; ++cc) rank1_tile(r0, cc, accA);
+    for (int cc = 0; cc < CT; ++cc) rank1_tile_prologue(r0, cc, accA);
   }
 #pragma unroll
   for (int b = 0; b < KB - 1; ++b)
@@ -703,7 +726,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
       // the previous chunk's y groups a short last chunk did not reach, before
       // the partials are overwritten
       const int done = min(max(ran - kSum0, 0), kGroups);
-      for (int i = done; i < kGroups; ++i) ysum_group((c - 1) * kChunk, tid + i * L::THREADS);
+      for (int i = done; i < kGroups; ++i) ysum_group((c - 1) * kChunk, tid + i * L::THREADS, ybuf(c - 1));
       lds_barrier();
     }
     const int te = ran - 2;  // the last pair: steps te, te + 1
@@ -714,9 +737,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < NRH; ++j) readout_mma(rl, bq, half, j);
     }
-    publish();
+    publish(ybuf(c));
     const int t0 = c * kChunk;
-    for (int grp = tid; grp < ns * (V / 4); grp += L::THREADS) ysum_group(t0, grp);
+    for (int grp = tid; grp < ns * (V / 4); grp += L::THREADS) ysum_group(t0, grp, ybuf(c));
   }
 
   if (a.HT) {
