@@ -39,12 +39,14 @@ METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
     # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
-    ("C3", "mfma"): (136485.5, 1056768.0, "m2rnn_mfma.hip",
-                     "1bc0c826cba1f59652c2940f5936aa56c2d4934b27d12aea700f6c8b1cf29904"),
+    ("C3", "mfma"): (136491.0, 1056768.0, "m2rnn_mfma.hip",
+                     "ccb2d9abe52490502a8ee23d990a795fe3ecfaebcc442ae56c927ab9d6632866"),
     ("D1", "mfma"): (267823.2, 530624.2, "m2rnn_decode.hip",
                      "956ca12e91e2af7f990630af4aead6a5a4ebb04ffc1229b7d6494d0c06ac9e4f"),
-    ("C5", "mfma_long_split"): (1053878.0, 2098176.0, "m2rnn_long.hip",
-                                "ce6094f04770b50e1f8726b4551d9001eb9c393746370b8de05fb13789e5c6bd"),
+    ("C4", "mfma_long_split"): (531636.6, 1050624.0, "m2rnn_long.hip",
+                                "97a72c73aba48752d64d5dc174f81cb23360bbd6541b3af24a2c68fb3816ccd3"),
+    ("C5", "mfma_long_split"): (1053876.5, 2098176.0, "m2rnn_long.hip",
+                                "97a72c73aba48752d64d5dc174f81cb23360bbd6541b3af24a2c68fb3816ccd3"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the

@@ -33,35 +33,15 @@
 // gate 1), which also apply the final update that turns G into dH0.
 #include <hip/hip_runtime.h>
 
+#include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f4;
-typedef __attribute__((ext_vector_type(2))) float f2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) short s4;
-typedef __attribute__((ext_vector_type(8))) short s8;
-typedef __attribute__((ext_vector_type(4))) unsigned int u4;
+using namespace dev;
 
-constexpr float kInvC = 0.34657359027997264f;  // ln 2 / 2
 constexpr int kChunk = 16;
-
-__device__ __forceinline__ float lo_bf16(unsigned int x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float hi_bf16(unsigned int x) { return __uint_as_float(x & 0xffff0000u); }
-__device__ __forceinline__ unsigned int pack_bf16(float x0, float x1) {
-  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f2{x0, x1}, bf16x2));
-}
-__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int V, int NW>
 struct BwdLayout {

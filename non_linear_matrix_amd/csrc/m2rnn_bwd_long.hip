@@ -30,57 +30,17 @@
 //     (gate 1, zero inputs) and turn G into dH0, as in the multi-step kernel.
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-#include <utility>
-
+#include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f4;
-typedef __attribute__((ext_vector_type(2))) float f2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) short s4;
-typedef __attribute__((ext_vector_type(8))) short s8;
-typedef __attribute__((ext_vector_type(4))) unsigned int u4;
+using namespace dev;
 
-constexpr float kInvC = 0.34657359027997264f;  // ln 2 / 2
 constexpr int kChunk = 16;
 constexpr int kAhead = 4;  // saved data loaded this many steps ahead
 constexpr int kRing = 8;   // ring slots (divides kChunk; > kAhead + 1)
-
-__device__ __forceinline__ float lo_bf16(unsigned int x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float hi_bf16(unsigned int x) { return __uint_as_float(x & 0xffff0000u); }
-__device__ __forceinline__ unsigned int pack_bf16(float x0, float x1) {
-  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f2{x0, x1}, bf16x2));
-}
-__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// sum over the 16 lanes of a DPP row; every lane of the row ends with the total
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // lane ^ 1
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // lane ^ 2
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half mirror
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // mirror
-  return x;
-}
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order
-template <typename F, int... S>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, S...>) {
-  (f(std::integral_constant<int, S>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 template <int V>
 struct BwdLongLayout {

@@ -27,38 +27,16 @@
 // Three workgroups per CU (LDS 43 KB, 128 VGPRs each) keep enough state reads in flight.
 #include <hip/hip_runtime.h>
 
+#include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f4;
-typedef __attribute__((ext_vector_type(8))) float f8;
-typedef __attribute__((ext_vector_type(4))) short s4;
-typedef __attribute__((ext_vector_type(8))) short s8;
-typedef __attribute__((ext_vector_type(4))) unsigned int u4;
-typedef __attribute__((ext_vector_type(2))) unsigned int u2;
+using namespace dev;
 
-constexpr float kC = 2.8853900817779268f;      // 2 / ln 2
-constexpr float kInvC = 0.34657359027997264f;  // ln 2 / 2
 constexpr int kThreads = 256;
 constexpr int kMaxItems = 8;                   // 16-row tiles handled per workgroup iteration
-
-__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf16_to_f32(unsigned int b) { return __uint_as_float(b << 16); }
-
-// sum over the 16 lanes of a DPP row; every lane of the row ends with the total
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // lane ^ 1
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // lane ^ 2
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half mirror
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // mirror
-  return x;
-}
 
 template <int V>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(FwdArgs a, int nsplit) {

@@ -39,34 +39,20 @@
 // loads are issued one chunk ahead into registers.
 #include <hip/hip_runtime.h>
 
+#include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 namespace {
 
+using namespace dev;
+
 constexpr int kChunk = 16;        // steps staged at once
 constexpr int kMaxThreads = 512;  // K = 128: 8 waves
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
+// D = A B + C on a 16x16 fp32 tile, A and B fp32 with 4-deep contraction
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
-                                                               false));
-}
-
-// Sum over the 16 lanes of a DPP row. Each stage adds a lane and its partner
-// (x + y and y + x are the same float), so every lane ends with the same value.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]: lane ^ 1
-  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
-  x += dpp<0x141>(x);  // row_half_mirror: the other quad of the half row
-  x += dpp<0x140>(x);  // row_mirror: the other half row
-  return x;
 }
 
 // LDS (floats): W fragments (V = 128 only: [co][c][lane] f4) | staged chunk
@@ -204,7 +190,7 @@ __global__ __launch_bounds__(kMaxThreads) void mfma_f32_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int co = 0; co < CT; ++co) acc[co] = mfma(wf[co][r], g[c][r], acc[co]);
+          for (int co = 0; co < CT; ++co) acc[co] = mfma4(wf[co][r], g[c][r], acc[co]);
       }
 #pragma unroll
       for (int co = 0; co < CT; ++co) {

@@ -24,16 +24,13 @@
 // tiles in flight within one XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f4;
-typedef __attribute__((ext_vector_type(2))) float f2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) unsigned int u4;
+using namespace dev;
 
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr int LROW = BK + 8;                   // bf16 per LDS row: 16 bytes of padding
@@ -51,10 +48,6 @@ struct FrontArgs {
   int N, D, T, H, K, V, R;
   int tiles_m, tiles_n;
 };
-
-__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ unsigned short to_bf16(float x) {
   const unsigned int p = __builtin_bit_cast(unsigned int, __builtin_convertvector(f2{x, 0.0f}, bf16x2));

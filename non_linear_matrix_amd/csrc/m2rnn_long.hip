@@ -30,50 +30,15 @@
 // fetched from HBM a chunk ahead.
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-#include <utility>
-
+#include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f4;
-typedef __attribute__((ext_vector_type(8))) float f8;
-typedef __attribute__((ext_vector_type(2))) float f2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) short s4;
-typedef __attribute__((ext_vector_type(8))) short s8;
-typedef __attribute__((ext_vector_type(4))) unsigned int u4;
+using namespace dev;
 
-constexpr float kC = 2.8853900817779268f;      // 2 / ln 2
-constexpr float kInvC = 0.34657359027997264f;  // ln 2 / 2
 constexpr int kChunk = 16;
-
-__device__ __forceinline__ float bf16_to_f32(unsigned int b) { return __uint_as_float(b << 16); }
-__device__ __forceinline__ unsigned int pack_bf16(float x0, float x1) {
-  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f2{x0, x1}, bf16x2));
-}
-__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// barrier that orders LDS only (global loads and y atomics stay in flight)
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order
-template <typename F, int... S>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, S...>) {
-  (f(std::integral_constant<int, S>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 template <int V>
 struct LongLayout {

@@ -56,31 +56,15 @@
 // loaded from HBM one chunk ahead of use.
 #include <hip/hip_runtime.h>
 
+#include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f4;
-typedef __attribute__((ext_vector_type(8))) float f8;
-typedef __attribute__((ext_vector_type(4))) short s4;
-typedef __attribute__((ext_vector_type(8))) short s8;
-typedef __attribute__((ext_vector_type(4))) unsigned int u4;
+using namespace dev;
 
-constexpr float kC = 2.8853900817779268f;      // 2 / ln 2
-constexpr float kInvC = 0.34657359027997264f;  // ln 2 / 2
 constexpr int kChunk = 16;                     // steps staged per LDS chunk
-
-__device__ __forceinline__ float bf16_to_f32(unsigned int b) { return __uint_as_float(b << 16); }
-
-typedef __attribute__((ext_vector_type(2))) float f2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-
-// two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32: round to nearest even)
-__device__ __forceinline__ unsigned int pack_bf16(float x0, float x1) {
-  return __builtin_bit_cast(unsigned int, __builtin_convertvector(f2{x0, x1}, bf16x2));
-}
 
 template <int V, int NW, bool SPLIT>
 struct Layout {
@@ -250,19 +234,6 @@ __device__ __forceinline__ void make_operand(const f4& g0, const f4& g1, bf16x8&
     }
     lo = __builtin_convertvector(r, bf16x8);
   }
-}
-
-// Workgroup barrier that orders LDS only. Global loads (the chunk prefetch) and
-// the atomic y updates stay in flight across it; a full __syncthreads would
-// wait for them, i.e. for a whole HBM round trip at every chunk end.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 template <int V, int NW, bool SPLIT, bool SAVE>
