@@ -40,13 +40,13 @@ COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
     # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
     ("C3", "mfma"): (136491.0, 1056768.0, "m2rnn_mfma.hip",
-                     "ccb2d9abe52490502a8ee23d990a795fe3ecfaebcc442ae56c927ab9d6632866"),
-    ("D1", "mfma"): (267823.2, 530624.2, "m2rnn_decode.hip",
-                     "956ca12e91e2af7f990630af4aead6a5a4ebb04ffc1229b7d6494d0c06ac9e4f"),
+                     "a26e52e6a73321c4ed31f50865d20295b65ac9a3a2ab196735b28cf8eafc21c6"),
+    ("D1", "mfma"): (267833.6, 530989.2, "m2rnn_decode.hip",
+                     "c6d1e2c83857babaa73de8959f8e68261b4615baddae8e54cd15d2d3191123b0"),
     ("C4", "mfma_long_split"): (531636.6, 1050624.0, "m2rnn_long.hip",
-                                "97a72c73aba48752d64d5dc174f81cb23360bbd6541b3af24a2c68fb3816ccd3"),
+                                "606f8a92fc678321323a19a345f1ed1d29ec2e989450c52018c2f0e95b757bc1"),
     ("C5", "mfma_long_split"): (1053876.5, 2098176.0, "m2rnn_long.hip",
-                                "97a72c73aba48752d64d5dc174f81cb23360bbd6541b3af24a2c68fb3816ccd3"),
+                                "606f8a92fc678321323a19a345f1ed1d29ec2e989450c52018c2f0e95b757bc1"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the
