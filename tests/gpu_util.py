@@ -108,6 +108,56 @@ def oracle_all_units(x, dtype: str, max_threads: int = 16) -> Tuple[np.ndarray, 
     return y, HT
 
 
+def bwd_oracle_all_units(x, dy, dtype: str, max_threads: int = 16, mem_budget: float = 48e9):
+    """The gradient oracle on every (b, h) unit of x, the units split over host
+    threads (as oracle_all_units; the thread count is also capped so the oracle's
+    per-step state histories fit in mem_budget bytes). dW of a head is the sum of
+    its batch rows' dW, added in batch order. Returns the oracle's dict with
+    every tensor at full shape."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle import m2rnn_bwd_ref
+
+    B, H, T, K = x["k"].shape
+    V = x["v"].shape[-1]
+    units = [(b, h) for b in range(B) for h in range(H)]
+    per_unit = 2.0 * (T + 1) * K * V * 8  # the states and tanh outputs the oracle keeps
+    cpus = max(1, min(os.cpu_count() or 1, max_threads))
+    n = max(1, min(cpus, len(units), int(mem_budget // per_unit)))
+
+    done = [0]
+
+    def one(u):
+        b, h = u
+        sub = {key: (None if a is None else (a[h:h + 1] if key == "W" else a[b:b + 1, h:h + 1]))
+               for key, a in x.items()}
+        out = m2rnn_bwd_ref(sub["k"], sub["v"], sub["q"], sub["f"], sub["W"], sub["H0"],
+                            dy[b:b + 1, h:h + 1], dtype=dtype)
+        done[0] += 1
+        if done[0] % max(1, len(units) // 8) == 0:
+            announce(f"gradient oracle: {done[0]} of {len(units)} units")
+        return out
+
+    with threadpool_limits(limits=max(1, cpus // n), user_api="blas"):
+        with ThreadPoolExecutor(max_workers=n) as pool:
+            outs = list(pool.map(one, units))
+    ref = {}
+    for key, a in outs[0].items():
+        if key == "dW":
+            ref[key] = np.zeros((H,) + a.shape[1:])
+        else:
+            ref[key] = np.empty((B, H) + a.shape[2:])
+    for (b, h), o in zip(units, outs):  # batch rows of a head in order b = 0, 1, ...
+        for key, a in o.items():
+            if key == "dW":
+                ref[key][h] += a[0]
+            else:
+                ref[key][b, h] = a[0, 0]
+    return ref
+
+
 _FULL: Dict[Tuple[str, int], tuple] = {}
 
 
