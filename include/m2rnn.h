@@ -94,16 +94,26 @@ typedef enum m2rnn_dtype {
  * AUTO:       fp32: MFMA_F32. bf16 with V in {64, 128}, T > 1 and at most
  *             768 16-row tiles (B H K / 16 <= 768; two workgroups fit per CU of
  *             a 256-CU gfx950): MFMA_LONG_SPLIT; else MFMA_SPLIT where it covers
- *             the shape, else SIMPLE. With M2RNN_FLAG_DETERMINISTIC it never takes
- *             MFMA_LONG*.
+ *             the shape, else SIMPLE. Every choice gives a bitwise repeatable y
+ *             onto a y the call clears; with M2RNN_FLAG_DETERMINISTIC and
+ *             M2RNN_FLAG_ACCUMULATE_Y together it avoids the families that add
+ *             two or more partial readouts into y.
  * MFMA_LONG, MFMA_LONG_SPLIT: the same arithmetic as MFMA / MFMA_SPLIT, for
  *             workloads with few 16-row tiles (B H K / 16 well below the GPU's
  *             1024 SIMDs: small batches, long sequences). Each tile's V columns
  *             are spread over V/32 waves that exchange the state operand through
  *             LDS every step, which cuts the per-step latency; each tile is its
  *             own workgroup, so y is summed over a unit's K/16 tiles with atomic
- *             adds whose order, and hence y's last bits, can vary between runs
- *             (H_T cannot). bf16, K in {16, ..., 128}, V in {64, 128}; the
+ *             adds. Each tile's contribution to y_t is first rounded to a grid of
+ *             spacing 2^(E-23), where 2^E > 1.0625 ||q_t||_1 M_t bounds |y_t|
+ *             (M_t: the bound on |H_t| from the gated convex update, M_0 =
+ *             max(1, max |H0|)); sums of such values are exact in fp32, so y does
+ *             not depend on the order of the adds (onto the y the call clears)
+ *             and is bitwise repeatable. The grid adds at most
+ *             2^-23 ||q_t||_1 M_t per tile to an element's error. The saving
+ *             forward of the training entry points adds unrounded sums (its y's
+ *             last bits can vary between runs; H_T and `saved` cannot).
+ *             bf16, K in {16, ..., 128}, V in {64, 128}; the
  *             training forwards take them for K in {32, 64, 128} (the shapes
  *             the backward pass covers) and write the same `saved` layout.
  *             MFMA_LONG has MFMA's precision (misses the bar on the same two
@@ -137,15 +147,17 @@ enum {
    * gets the plain result with the recurrence as the only kernel on the stream. */
   M2RNN_FLAG_ACCUMULATE_Y = 1u,
   /* Every output bitwise repeatable from run to run. H_T always is; y is
-   * whenever each element receives at most one atomic contribution, or two onto
-   * a y the call cleared itself. The families that add partial readouts into y
-   * atomically are MFMA and MFMA_SPLIT at K = 128 (two workgroups per unit) and
+   * whenever each element receives at most one atomic contribution, two onto a
+   * y the call cleared itself, or the long families' grid-rounded contributions
+   * onto a y the call cleared itself. The families that add partial readouts into
+   * y atomically are MFMA and MFMA_SPLIT at K = 128 (two workgroups per unit) and
    * MFMA_LONG* with T > 1 (K/16 row tiles per unit; T = 1 on the matrix-core
-   * shapes runs the decoding kernel, which has no atomics). Under this flag AUTO
-   * keeps to a combination that is repeatable (MFMA_SPLIT in place of
-   * MFMA_LONG_SPLIT, SIMPLE where nothing else is), and an explicit family that
-   * is not (three or more adds per element, or two together with
-   * M2RNN_FLAG_ACCUMULATE_Y) is NOT_SUPPORTED. */
+   * shapes runs the decoding kernel, which has no atomics). So only together
+   * with M2RNN_FLAG_ACCUMULATE_Y does this flag change anything: AUTO then keeps
+   * to a repeatable combination (MFMA_SPLIT in place of MFMA_LONG_SPLIT where it
+   * has one workgroup per unit, SIMPLE where nothing else is), and an explicit
+   * family that adds two or more contributions into the caller's y is
+   * NOT_SUPPORTED. */
   M2RNN_FLAG_DETERMINISTIC = 2u
 };
 
@@ -360,7 +372,8 @@ const char* m2rnn_status_string(m2rnn_status status);
  * m2rnn_fwd_varlen and the training entry points, 0.3.0 the recomputing ones and the front-end, 0.4.0 MFMA_LONG, 0.5.0 AUTO's
  * choice of MFMA_LONG_SPLIT and M2RNN_FLAG_DETERMINISTIC, 0.6.0 MFMA_LONG* in
  * the training forwards and m2rnn_bwd_algo, 0.7.0 m2rnn_get_plan_ex and
- * m2rnn_bwd_noalloc, 0.8.0 MFMA_F32). */
+ * m2rnn_bwd_noalloc, 0.8.0 MFMA_F32, 0.9.0 the grid-rounded, order-independent y of
+ * MFMA_LONG*). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

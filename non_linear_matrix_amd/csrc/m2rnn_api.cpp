@@ -80,19 +80,22 @@ m2rnn_status training_algo(m2rnn_algo& algo, int B, int H, int T, int K, int V, 
 bool is_long(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT; }
 bool is_split(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_SPLIT || algo == M2RNN_ALGO_MFMA_LONG_SPLIT; }
 
-// Whether a forward call's y has one fixed summation order (bitwise repeatable).
-// Kernels whose workgroups share a unit add their readouts into y atomically:
-// the multi-step kernels' K/(16 NW) workgroups and the long kernels' K/16 row
-// tiles. One contribution per element, or two onto a cleared y (0 + a + b =
-// 0 + b + a exactly), cannot depend on the order; two onto a y that already holds
-// values (M2RNN_FLAG_ACCUMULATE_Y) or three and more can. One step on the
-// matrix-core shapes runs the decoding kernel, which sums in LDS in a fixed order.
+// Whether a forward call's y is bitwise repeatable (the order of its atomic adds
+// cannot change it). Kernels whose workgroups share a unit add their readouts
+// into y atomically: the multi-step kernels' K/(16 NW) workgroups and the long
+// kernels' K/16 row tiles. One contribution per element, or two onto a cleared y
+// (0 + a + b = 0 + b + a exactly), cannot depend on the order. The long kernels
+// round every contribution to a grid on which all the sums are exact, so any
+// number of them onto a cleared y is repeatable. Adds onto a y that already holds
+// values (M2RNN_FLAG_ACCUMULATE_Y) from two workgroups or more are not. One step
+// on the matrix-core shapes runs the decoding kernel, which sums in LDS in a
+// fixed order.
 bool atomic_free(m2rnn_algo algo, int T, int K, int V, bool bf16, bool accumulate) {
   int adds = 1;
   const bool decode = T == 1 && m2rnn::mfma_supports(K, V, bf16);
   if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT) adds = decode ? 1 : m2rnn::mfma_groups(K);
   if (is_long(algo)) adds = decode ? 1 : K / 16;
-  return adds <= 1 || (adds == 2 && !accumulate);
+  return adds <= 1 || (!accumulate && (adds == 2 || is_long(algo)));
 }
 
 // The kernel family a forward call runs: AUTO resolved, and the rules of the
@@ -408,6 +411,6 @@ const char* m2rnn_status_string(m2rnn_status status) {
   }
 }
 
-int m2rnn_version(void) { return 800; }
+int m2rnn_version(void) { return 900; }
 
 }  // extern "C"

@@ -24,8 +24,16 @@
 //     reads, one MFMA per 16 columns per step pair against q; every 16 steps a
 //     wave adds its columns' sums over the tile's 16 rows into y with atomic
 //     adds. The K/16 row tiles of a unit are separate workgroups, so y receives
-//     K/16 contributions per element in an order that can vary between runs
-//     (rounding-level differences); H_T does not depend on any order.
+//     K/16 contributions per element in an order that varies between runs. Each
+//     contribution is first rounded to a grid of spacing 2^(E_t - 23), where
+//     2^E_t bounds |y_t| from quantities every workgroup of the unit computes
+//     identically: ||q_t||_1 over all K rows times M, a bound on |H_t| that the
+//     gated convex update gives (|tanh| <= 1, so M_t = f_t M_{t-1} + 1 - f_t
+//     from M_0 = max(1, max |H0|) bounds it; M_t never grows, so the bound at a
+//     chunk's start serves all its steps). Every sum of such values is a
+//     multiple of the spacing below 2^(E_t + 1), so it is exact in fp32 and the
+//     order of the adds cannot change y (onto a cleared y). The grid adds at
+//     most 2^-23 ||q_t||_1 M per row tile to an element's error.
 // Inputs k, v, q, f are staged per 16-step chunk into LDS (two stage buffers),
 // fetched from HBM a chunk ahead.
 #include <hip/hip_runtime.h>
@@ -40,7 +48,10 @@ using namespace dev;
 
 constexpr int kChunk = 16;
 
-template <int V>
+// GRID: the y grid of the plain forward (the training forward keeps its y adds
+// unrounded and stages only its own rows of q, which keeps it within the
+// registers of two workgroups per CU).
+template <int V, bool GRID>
 struct LongLayout {
   static constexpr int S = V / 32;        // waves per workgroup = column blocks
   static constexpr int CT = V / 16;       // 16-column tiles
@@ -63,24 +74,47 @@ struct LongLayout {
   static constexpr int YS_ROW = 33;       // floats per row of a wave's y transpose tile
   static constexpr int YS_BYTES = S * 16 * YS_ROW * 4;
   static constexpr int YS_OFF = XL_OFF + XL_BYTES;
-  static constexpr int Z_OFF = YS_OFF + YS_BYTES;
+  // the y-grid inputs of the last four staged chunks (index chunk & 3): ||q_t||_1
+  // over all K rows per step, and the state bound M for the chunk's steps
+  static constexpr int YB_SLOTS = 4;
+  static constexpr int YB_PER = kChunk + 4;
+  static constexpr int YB_BYTES = YB_SLOTS * YB_PER * 4;
+  static constexpr int YB_OFF = YS_OFF + YS_BYTES;
+  static constexpr int Z_OFF = YB_OFF + YB_BYTES;
   static constexpr int TOTAL = Z_OFF + 16;
   static_assert(V * HROW * 2 <= VX_BYTES, "W fits in the rank-1 region during the prologue");
-  static_assert(TOTAL <= 160 * 1024, "LDS budget");
-  // 16-byte global pieces of one chunk
-  static constexpr int P_K = kChunk * 2;        // 16 rows of k per step: 2 pieces
-  static constexpr int P_Q = kChunk * 2;
+  static_assert(2 * TOTAL <= 160 * 1024, "two workgroups per CU");
+  // 16-byte global pieces of one chunk: k of the tile's 16 rows, q of them
+  // (without GRID), v
+  static constexpr int P_K = kChunk * 2;
+  static constexpr int P_Q = GRID ? 0 : kChunk * 2;
   static constexpr int P_V = kChunk * V / 8;
   static constexpr int PIECES = P_K + P_Q + P_V;
   static constexpr int PPT = (PIECES + THREADS - 1) / THREADS;
+  // GRID: q of every row (K <= 128: 16 pieces per step), its own registers. Piece
+  // i = tid + j THREADS is step i / 16, part i % 16, so a step's pieces fill one
+  // 16-lane DPP row.
+  static constexpr int QPT = GRID ? kChunk * 16 / THREADS : 0;
+  static_assert(!GRID || QPT * THREADS == kChunk * 16, "whole q pieces per thread");
 };
+
+// Product over the 16 lanes of a DPP row; every lane of the row ends with it
+// (each stage multiplies a lane by its partner: x y and y x are the same float).
+__device__ __forceinline__ float row_prod16(float x) {
+  x *= __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  x *= __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  x *= __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half mirror
+  x *= __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // mirror
+  return x;
+}
 
 // One chunk of per-step inputs for the tile's 16 rows: loaded to registers, then
 // stored into a stage buffer in the forms the MFMAs read.
-template <int V>
+template <int V, bool GRID>
 struct LongStager {
-  using L = LongLayout<V>;
+  using L = LongLayout<V, GRID>;
   u4 reg[L::PPT];
+  u4 qreg[L::QPT > 0 ? L::QPT : 1];
   unsigned short freg;
 
   __device__ __forceinline__ void load(const FwdArgs& a, long long unit, int row0, int chunk, int Tb,
@@ -106,12 +140,52 @@ struct LongStager {
         if (t < Tb) reg[p] = *reinterpret_cast<const u4*>(v + (unit * ld + t) * V + 8 * part);
       }
     }
+    if constexpr (GRID) {
+#pragma unroll
+      for (int j = 0; j < L::QPT; ++j) {
+        const int i = tid + j * L::THREADS, t = t0 + i / 16, col = 8 * (i % 16);
+        qreg[j] = u4{0, 0, 0, 0};
+        if (t < Tb && col < a.K) qreg[j] = *reinterpret_cast<const u4*>(q + (unit * ld + t) * a.K + col);
+      }
+    }
     freg = 0x3f80u;  // gate 1 past the end: the padding steps keep the state
     if (tid < kChunk && t0 + tid < Tb) freg = f[unit * ld + t0 + tid];
   }
 
-  __device__ __forceinline__ void store(char* lds, int buf) const {
+  // Publish chunk `chunk` into stage buffer chunk & 1, and with GRID its y-grid
+  // inputs into slot chunk & 3: ||q_t||_1 per step (each step's 16 pieces summed
+  // over one DPP row in a fixed order) and the state bound M for the chunk's
+  // steps; m carries the bound from chunk to chunk (wave 0). Every workgroup of
+  // the unit computes the same values.
+  __device__ __forceinline__ void store(char* lds, int chunk, int row0, float& m) const {
     const int tid = threadIdx.x;
+    const int buf = chunk & 1;
+    float* yb = reinterpret_cast<float*>(lds + L::YB_OFF) + (chunk & (L::YB_SLOTS - 1)) * L::YB_PER;
+    if constexpr (GRID) {
+    unsigned short* qsg = reinterpret_cast<unsigned short*>(lds + L::QS_OFF) + buf * kChunk * 16;
+#pragma unroll
+    for (int j = 0; j < L::QPT; ++j) {
+      const int i = tid + j * L::THREADS, st = i / 16, own = i % 16 - row0 / 8;
+      float qa = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        qa += fabsf(bf16_to_f32(qreg[j][d] & 0xffffu)) + fabsf(bf16_to_f32(qreg[j][d] >> 16));
+      qa = row_sum16(qa);
+      if (i % 16 == 0) yb[st] = qa;
+      // the tile's own rows are the readout's q
+      if (own == 0 || own == 1) *reinterpret_cast<u4*>(qsg + st * 16 + 8 * own) = qreg[j];
+    }
+    if (tid < 64) {
+      // M_t - 1 = f_t (M_{t-1} - 1) and M >= 1, so M is non-increasing: the bound
+      // at the chunk's start holds for all its steps, and after the chunk it is
+      // 1 + (f_0 ... f_15)(M - 1). The product runs over the DPP row of lanes
+      // 0 .. 15, which hold the chunk's gates (1 past the sequence's end).
+      float pf = row_prod16(bf16_to_f32(freg));
+      pf = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pf), 0));
+      if (tid == 0) yb[kChunk] = m;
+      m = fmaf(pf, m - 1.0f, 1.0f);
+    }
+    }
     unsigned int* kx = reinterpret_cast<unsigned int*>(lds + L::KX_OFF) + buf * kChunk * 16;
     unsigned short* qs = reinterpret_cast<unsigned short*>(lds + L::QS_OFF) + buf * kChunk * 16;
     float* fs = reinterpret_cast<float*>(lds + L::FS_OFF) + buf * kChunk * 4;
@@ -158,8 +232,10 @@ struct LongStager {
 };
 
 template <int V, bool SPLIT, bool SAVE>
-__global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kernel(FwdArgs a) {
-  using L = LongLayout<V>;
+__global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs a) {
+  constexpr bool GRID = !SAVE;
+  using L = LongLayout<V, GRID>;
+  static_assert(L::THREADS == 64 * (V / 32), "launch bounds");
   constexpr int KB = V / 32, HROW = L::HROW, NHS = L::NHS;
   __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
 
@@ -184,7 +260,7 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
   const unsigned int* zero_lds = reinterpret_cast<const unsigned int*>(lds + L::Z_OFF);
 
   // ---- prologue: chunk 0/1 inputs, W, H0 requested before the first wait
-  LongStager<V> st, st1;
+  LongStager<V, GRID> st, st1;
   st.load(a, unit, row0, 0, Tb, LD);
   if (nchunks > 1) st1.load(a, unit, row0, 1, Tb, LD);
   constexpr int WLOADS = V * V / 8 / L::THREADS;
@@ -194,6 +270,24 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
     const u4* Wg = reinterpret_cast<const u4*>(static_cast<const unsigned short*>(a.W) + (long long)h * V * V);
 #pragma unroll
     for (int p = 0; p < WLOADS; ++p) wreg[p] = Wg[tid + p * L::THREADS];
+  }
+  // the y grid's state bound M_0 = max(1, max |H0|) over the unit's whole H0
+  // (every workgroup of the unit reads all of it: max does not round, so all
+  // get the same value)
+  float hmax = 0.0f;
+  if (GRID && a.H0 && a.y) {
+    const f4* h0u = reinterpret_cast<const f4*>(a.H0 + unit * a.K * V);
+#pragma unroll 1
+    for (int i = tid; i < a.K * V / 4; i += L::THREADS) {
+      const f4 hv = h0u[i];
+      hmax = fmaxf(hmax, fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3]))));
+    }
+  }
+  float* const ybt = reinterpret_cast<float*>(lds + L::YB_OFF);
+  if constexpr (GRID) {
+#pragma unroll
+    for (int off = 32; off >= 1; off /= 2) hmax = fmaxf(hmax, __shfl_xor(hmax, off));
+    if (l == 0) ybt[w] = hmax;  // read after the W-staging barrier below
   }
   f4 G[2];  // own output tiles 2w, 2w + 1: lane (g, n) holds G[n][16 c + 4 g + i]
   {
@@ -219,6 +313,8 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
       *reinterpret_cast<u4*>(wst + (i / (V / 8)) * HROW + 8 * (i % (V / 8))) = wreg[p];
     }
     __syncthreads();
+    if constexpr (GRID)
+      for (int ww = 0; ww < L::S; ++ww) hmax = fmaxf(hmax, ybt[ww]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -240,8 +336,11 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
       *reinterpret_cast<uint2*>(reinterpret_cast<unsigned int*>(lds + L::VX_OFF) + i * L::NVX + 4 * k + 2) =
           uint2{0u, 0u};
   if (tid < 4) reinterpret_cast<unsigned int*>(lds + L::Z_OFF)[tid] = 0u;
-  if (nchunks > 0) st.store(lds, 0);
-  if (nchunks > 1) st1.store(lds, 1);
+  // the y grid's state bound: after the last staged chunk (wave 0), and per step
+  // of that chunk (lanes 0 .. 15)
+  float mbound = fmaxf(1.0f, hmax);
+  if (nchunks > 0) st.store(lds, 0, row0, mbound);
+  if (nchunks > 1) st1.store(lds, 1, row0, mbound);
   if (nchunks > 2) st.load(a, unit, row0, 2, Tb, LD);
 
   // operand blocks: Bf[o] lane (g, n) = bf16 G[n][32 b + 16 (j / 4) + 4 g + j % 4],
@@ -352,10 +451,22 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
     if (a.y != nullptr && pend_n > 0) {
       // through the wave's own LDS tile, so that each add instruction covers two
       // rows of 32 consecutive floats
+      // lane (g, n) holds sums of step row n: each goes onto that step's grid of
+      // spacing 2^(E - 23) (every sum of such values below 2^(E + 1) is exact)
+      // (the training forward adds its sums unrounded)
+      // E from the step's ||q_t||_1 and the chunk's state bound, with a sixteenth
+      // of headroom for the rounding of the bound itself and of the bf16 readout
+      // operand: 2^E > 1.0625 ||q_t||_1 M
+      const float* ybp = ybt + ((pend_t0 / kChunk) & (L::YB_SLOTS - 1)) * L::YB_PER;
+      const int e = GRID ? __builtin_amdgcn_frexp_expf(ybp[n] * ybp[kChunk] * 1.0625f) : 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ys[n * L::YS_ROW + 16 * (g % 2) + 8 * j + 4 * (g / 2) + i] = Dp[j][i] * kInvC;
+        for (int i = 0; i < 4; ++i) {
+          float x = Dp[j][i] * kInvC;
+          if constexpr (GRID) x = __builtin_amdgcn_ldexpf(__builtin_rintf(__builtin_amdgcn_ldexpf(x, 23 - e)), e - 23);
+          ys[n * L::YS_ROW + 16 * (g % 2) + 8 * j + 4 * (g / 2) + i] = x;
+        }
       __builtin_amdgcn_wave_barrier();
       // every value first, then the adds with no branch between them: a row
       // past the sequence's end adds zero to the chunk's last valid row (x + 0
@@ -456,7 +567,7 @@ __global__ __launch_bounds__(LongLayout<V>::THREADS, 1) void mfma_fwd_long_kerne
         // stages chunk c + 1 into chunk c - 1's buffer (its last reads were
         // before this step's barrier) and fetches chunk c + 2
         if (c >= 1 && c + 1 < nchunks) {
-          st.store(lds, (c + 1) & 1);
+          st.store(lds, c + 1, row0, mbound);
           if (c + 2 < nchunks) st.load(a, unit, row0, c + 2, Tb, LD);
         }
         add_y();  // chunk c - 1's sums
@@ -491,7 +602,7 @@ bool long_supports(const FwdArgs& a) {
 Plan plan_long(int B, int H, int K, int V) {
   const long long grid = (long long)B * H * (K / 16);
   return Plan{grid > 0x7fffffffLL ? -1 : (int)grid, 64 * (V / 32), 16, K / 16, 1,
-              V == 128 ? LongLayout<128>::TOTAL : LongLayout<64>::TOTAL};
+              V == 128 ? LongLayout<128, true>::TOTAL : LongLayout<64, true>::TOTAL};
 }
 
 hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream) {

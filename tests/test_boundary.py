@@ -28,7 +28,7 @@ def _check(**over):
 def test_library_exists_and_loads():
     assert os.path.exists(m2rnn.LIB_PATH), "build the library first (python -m non_linear_matrix_amd.build)"
     lib = m2rnn.load()
-    assert m2rnn.version() == 800
+    assert m2rnn.version() == 900
 
 
 def test_every_declared_symbol_is_exported():
@@ -167,35 +167,43 @@ def test_auto_picks_a_kernel_that_covers_the_shape():
     assert p["algo"] == "mfma_long_split" and p["grid"] == 256 and p["block"] == 256 and p["clears_y"] == 1
 
 
-def test_deterministic_flag_refuses_the_atomic_kernels():
-    """M2RNN_FLAG_DETERMINISTIC: explicit MFMA_LONG* with T > 1 is refused before
-    any launch (their y adds over row tiles are atomic)."""
+def test_deterministic_flag_and_the_long_kernels():
+    """M2RNN_FLAG_DETERMINISTIC: the long kernels round each row tile's readout
+    onto a common grid, so their y is repeatable onto the y the call clears (any
+    number of row tiles) and they are accepted; adding into the caller's y from
+    two or more row tiles is refused before any launch."""
     lib = m2rnn.load()
-    det = m2rnn.FLAG_DETERMINISTIC
+    det, acc = m2rnn.FLAG_DETERMINISTIC, m2rnn.FLAG_ACCUMULATE_Y
     for algo in ("mfma_long", "mfma_long_split"):
-        st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 2, 16, 64, 128, 1, m2rnn.ALGOS[algo], det, None)
+        for K in (16, 64, 128):
+            st = lib.m2rnn_check_args(A, A, A, A, A, None, A, None, 1, 2, 16, K, 128, 1, m2rnn.ALGOS[algo])
+            assert st == OK
+            assert m2rnn.get_plan(1, 2, 16, K, 128, "bf16", algo, det)["algo"] == algo, (algo, K)
+        st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 2, 16, 64, 128, 1, m2rnn.ALGOS[algo], det | acc, None)
         assert st == UNSUPPORTED, algo
-        st = lib.m2rnn_fwd_ex(A, A, A, A, A, None, A, None, 1, 2, 16, 64, 128, 1, m2rnn.ALGOS[algo],
-                              det | m2rnn.FLAG_ACCUMULATE_Y, None)
-        assert st == UNSUPPORTED, algo
+        # one row tile: a single add per element, accumulation included
+        assert m2rnn.get_plan(1, 2, 16, 16, 128, "bf16", algo, det | acc)["algo"] == algo
 
 
 def test_deterministic_auto_resolves_to_a_covering_repeatable_kernel():
-    """AUTO under M2RNN_FLAG_DETERMINISTIC leaves the long kernel for the
-    multi-step split kernel only where that kernel covers the shape (else the
-    simple kernel), and never keeps a kernel that would add into y atomically
-    in an order-dependent way. Host only: the plan query launches nothing."""
+    """AUTO under M2RNN_FLAG_DETERMINISTIC keeps its choice unless the call also
+    accumulates into y from two or more workgroups: then it takes the multi-step
+    split kernel where that has one workgroup per unit, else the simple kernel.
+    Host only: the plan query launches nothing."""
     det, acc = m2rnn.FLAG_DETERMINISTIC, m2rnn.FLAG_ACCUMULATE_Y
-    # K not covered by the multi-step kernel: the simple kernel (it once resolved
-    # to MFMA_SPLIT, which then refused the shape at launch)
-    for K in (48, 80, 96, 112):
-        assert m2rnn.get_plan(2, 3, 37, K, 128, "bf16", "auto", det)["algo"] == "simple", K
-    assert m2rnn.get_plan(2, 3, 37, 64, 128, "bf16", "auto", det)["algo"] == "mfma_split"
-    # one or two row tiles onto a cleared y stay on the long kernel
-    assert m2rnn.get_plan(2, 3, 37, 16, 128, "bf16", "auto", det)["algo"] == "mfma_long_split"
-    assert m2rnn.get_plan(2, 3, 37, 32, 128, "bf16", "auto", det)["algo"] == "mfma_long_split"
+    # the long kernel stays under the flag alone, for every K
+    for K in (16, 32, 48, 64, 80, 96, 112, 128):
+        assert m2rnn.get_plan(2, 3, 37, K, 128, "bf16", "auto", det)["algo"] == "mfma_long_split", K
+    assert m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "auto", det)["algo"] == "mfma_long_split"
+    # accumulating: the multi-step kernel where it runs one workgroup per unit
     assert m2rnn.get_plan(2, 3, 37, 32, 128, "bf16", "auto", det | acc)["algo"] == "mfma_split"
-    # K = 128 on the multi-step kernel: two workgroups add into y
+    assert m2rnn.get_plan(2, 3, 37, 64, 128, "bf16", "auto", det | acc)["algo"] == "mfma_split"
+    # ... and the simple kernel where it does not cover the shape (K = 48, ...) or
+    # runs two workgroups (K = 128); one row tile stays on the long kernel
+    for K in (48, 80, 96, 112, 128):
+        assert m2rnn.get_plan(2, 3, 37, K, 128, "bf16", "auto", det | acc)["algo"] == "simple", K
+    assert m2rnn.get_plan(2, 3, 37, 16, 128, "bf16", "auto", det | acc)["algo"] == "mfma_long_split"
+    # K = 128 on the multi-step kernel: two workgroups add into a cleared y
     assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", det)["algo"] == "mfma_split"
     assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", det | acc)["algo"] == "simple"
     # without the flag nothing changes
@@ -220,8 +228,7 @@ def test_deterministic_accumulate_refuses_two_atomic_groups():
         assert m2rnn.get_plan(2, 2, 1, 128, 128, "bf16", algo, det | acc)["algo"] == algo
         assert m2rnn.get_plan(2, 2, 40, 128, 128, "bf16", algo, det)["algo"] == algo
     for algo in ("mfma_long", "mfma_long_split"):
-        with pytest.raises(m2rnn.M2RNNError):
-            m2rnn.get_plan(2, 2, 40, 48, 128, "bf16", algo, det)
+        assert m2rnn.get_plan(2, 2, 40, 48, 128, "bf16", algo, det)["algo"] == algo
         assert m2rnn.get_plan(2, 2, 40, 32, 128, "bf16", algo, det)["algo"] == algo
         with pytest.raises(m2rnn.M2RNNError):
             m2rnn.get_plan(2, 2, 40, 32, 128, "bf16", algo, det | acc)

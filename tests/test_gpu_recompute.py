@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from gpu_util import announce, nerr, to_device
-from non_linear_matrix_amd.inputs import CONFIGS, generate, scaled
+from non_linear_matrix_amd.inputs import CONFIGS, bf16_bits_to_fp32, generate, scaled
 from oracle import m2rnn_bwd_ref, m2rnn_fwd_ref
 
 pytestmark = pytest.mark.gpu
@@ -116,9 +116,14 @@ def test_one_segment_equals_the_saved_state_backward_bit_for_bit():
     torch.cuda.synchronize()
     assert ck is None
     assert torch.equal(H1, H2)
-    # y: the latency-oriented forward (AUTO here) sums it over row tiles with
-    # atomic adds, so only to rounding
-    assert (y1 - y2).abs().max().item() <= 1e-6 * y1.abs().max().item()
+    # y: the latency-oriented forward (AUTO here) sums it over its K/16 row tiles;
+    # the plain forward first rounds each tile's sum onto a grid of spacing
+    # 2^(E - 23) with 2^E < 2.125 ||q_t||_1 (here max|H0| < 1), the saving forward
+    # does not: they differ by at most K/16 half-spacings per element
+    K = cfg.K
+    qn = bf16_bits_to_fp32(x["q"]).astype(np.float64)
+    bound = (K // 16) * 2.0 ** -24 * 2.125 * float(np.max(np.sum(np.abs(qn), axis=-1)))
+    assert (y1 - y2).abs().max().item() <= bound
     for key in GRADS:
         assert torch.equal(g1[key], g2[key]), key
 
