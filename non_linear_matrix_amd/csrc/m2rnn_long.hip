@@ -273,14 +273,18 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   }
   // the y grid's state bound M_0 = max(1, max |H0|) over the unit's whole H0
   // (every workgroup of the unit reads all of it: max does not round, so all
-  // get the same value)
+  // get the same value); four loads in flight per thread
   float hmax = 0.0f;
   if (GRID && a.H0 && a.y) {
     const f4* h0u = reinterpret_cast<const f4*>(a.H0 + unit * a.K * V);
-#pragma unroll 1
-    for (int i = tid; i < a.K * V / 4; i += L::THREADS) {
-      const f4 hv = h0u[i];
-      hmax = fmaxf(hmax, fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3]))));
+    const int n4 = a.K * V / 4;
+    for (int i = tid; i < n4; i += 4 * L::THREADS) {
+      f4 hv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) hv[u] = i + u * L::THREADS < n4 ? h0u[i + u * L::THREADS] : f4{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        hmax = fmaxf(hmax, fmaxf(fmaxf(fabsf(hv[u][0]), fabsf(hv[u][1])), fmaxf(fabsf(hv[u][2]), fabsf(hv[u][3]))));
     }
   }
   float* const ybt = reinterpret_cast<float*>(lds + L::YB_OFF);

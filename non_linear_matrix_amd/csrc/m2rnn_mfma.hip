@@ -421,25 +421,49 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   float* y = a.y;
   const bool atomic_y = splits > 1 || a.accumulate;
 
-  // y of one group (a step and 4 positions) of the chunk starting at t0, from the
-  // waves' partials in partial buffer yb, added in wave order
+  // y of one group (a step and 4 columns) of the chunk starting at t0, from the
+  // waves' partials in partial buffer yb, added in wave order. The partials sit
+  // in the permuted order of the readout: position 16 P + 4 gg + i holds column
+  // 32 (P/2) + 16 (gg%2) + 8 (P%2) + 4 (gg/2) + i.
   auto ysum_group = [&](int t0, int grp, int yb) {
     const float* ypb = yp_all + yb * NW * kChunk * L::YROW;
-    const int sn = grp / (V / 4), pos = 4 * (grp % (V / 4));
-    f4 sum = *reinterpret_cast<const f4*>(ypb + sn * L::YROW + pos);
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(ypb + (ww * kChunk + sn) * L::YROW + pos);
-    sum *= kInvC;
-    // position 16 P + 4 gg  ->  column 32 (P/2) + 16 (gg%2) + 8 (P%2) + 4 (gg/2)
-    const int P = pos / 16, gg = (pos % 16) / 4;
-    const int col = 32 * (P / 2) + 16 * (gg % 2) + 8 * (P % 2) + 4 * (gg / 2);
+    const int sn = grp / (V / 4), j = grp % (V / 4);
     if (y == nullptr) return;  // states recomputed for the backward pass: no readout wanted
-    float* dst = y + (unit * LD + t0 + sn) * V + col;
-    if (atomic_y) {
+    // (the split-operand and saving forwards keep one 16-byte group per lane for
+    // their atomic adds too: the column-spread adds below cost those kernels
+    // more LDS reads and registers than the write traffic they save; measured
+    // 1.3% slower with the split operand)
+    if (!atomic_y || SAVE || SPLIT) {
+      // four consecutive columns, one 16-byte store
+      const int pos = 4 * j;
+      f4 sum = *reinterpret_cast<const f4*>(ypb + sn * L::YROW + pos);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, sum[i]);
-    } else {
-      *reinterpret_cast<f4*>(dst) = sum;
+      for (int ww = 1; ww < NW; ++ww) sum += *reinterpret_cast<const f4*>(ypb + (ww * kChunk + sn) * L::YROW + pos);
+      sum *= kInvC;
+      const int P = pos / 16, gg = (pos % 16) / 4;
+      const int col = 32 * (P / 2) + 16 * (gg % 2) + 8 * (P % 2) + 4 * (gg / 2);
+      float* dst = y + (unit * LD + t0 + sn) * V + col;
+      if (atomic_y) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, sum[i]);
+      } else {
+        *reinterpret_cast<f4*>(dst) = sum;
+      }
+      return;
+    }
+    // atomic adds: columns j, j + V/4, j + V/2, j + 3V/4, so that consecutive
+    // threads add into consecutive floats and each add instruction covers whole
+    // 128-byte rows of y (with four consecutive floats per lane each 4-byte add
+    // rewrote a 16-byte piece of memory: 3.9x the HBM writes at C3)
+    float* dst = y + (unit * LD + t0 + sn) * V;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = j + (V / 4) * i, r = col % 32;
+      const int pos = 16 * (2 * (col / 32) + (r % 16) / 8) + 4 * (2 * ((r % 8) / 4) + r / 16) + r % 4;
+      float sum = ypb[sn * L::YROW + pos];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) sum += ypb[(ww * kChunk + sn) * L::YROW + pos];
+      unsafeAtomicAdd(dst + col, sum * kInvC);
     }
   };
 

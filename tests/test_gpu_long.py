@@ -143,6 +143,22 @@ def test_auto_takes_the_long_kernel_and_is_repeatable():
     assert np.array_equal(y1, y2) and np.array_equal(H1, H2)
 
 
+@pytest.mark.parametrize("K", [16, 48, 128])
+def test_repeatable_with_a_large_initial_state(K):
+    """The y grid's state bound starts at max |H0| when that exceeds 1 and decays
+    with the gates: with H0 ~ U(-40, 40) y is still the same bit for bit from run
+    to run and within the bar of the oracle (K = 16: one row tile, K = 48: three)."""
+    cfg = scaled(CONFIGS["C5"], B=1, H=3, K=K, T=90)
+    announce(f"large H0, K={K}")
+    x = generate(cfg, 68)
+    x["H0"] = (np.random.default_rng(69).uniform(-40, 40, (1, 3, K, cfg.V))).astype(np.float32)
+    y1, H1 = gpu_run(x, algo="mfma_long_split")
+    y2, H2 = gpu_run(x, algo="mfma_long_split")
+    assert np.array_equal(y1, y2) and np.array_equal(H1, H2)
+    yr, HTr = oracle_units(x, "bf16")
+    assert nerr(y1, yr) <= TOL and nerr(H1, HTr) <= TOL
+
+
 @pytest.mark.parametrize("name", ["C2", "C4", "C5"])
 def test_default_forward_is_bitwise_repeatable(name):
     """The library's default forward (AUTO: the split long kernel on these
