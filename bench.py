@@ -39,14 +39,14 @@ METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
     # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
-    ("C3", "mfma"): (136491.0, 1056768.0, "m2rnn_mfma.hip",
-                     "a26e52e6a73321c4ed31f50865d20295b65ac9a3a2ab196735b28cf8eafc21c6"),
+    ("C3", "mfma"): (136498.3, 270336.0, "m2rnn_mfma.hip",
+                     "97d64cc4358e5944ff6b0f11ebc2f377ad5ce89e24ab16cb684b68deb364244a"),
     ("D1", "mfma"): (267833.6, 530989.2, "m2rnn_decode.hip",
                      "c6d1e2c83857babaa73de8959f8e68261b4615baddae8e54cd15d2d3191123b0"),
-    ("C4", "mfma_long_split"): (531636.6, 1050624.0, "m2rnn_long.hip",
-                                "606f8a92fc678321323a19a345f1ed1d29ec2e989450c52018c2f0e95b757bc1"),
-    ("C5", "mfma_long_split"): (1053876.5, 2098176.0, "m2rnn_long.hip",
-                                "606f8a92fc678321323a19a345f1ed1d29ec2e989450c52018c2f0e95b757bc1"),
+    ("C4", "mfma_long_split"): (669899.6, 1050624.0, "m2rnn_long.hip",
+                                "5f3abb56d979ba104a26c69660f21374199565dcfbf10d2ec035902364c848b6"),
+    ("C5", "mfma_long_split"): (1053893.5, 2098176.0, "m2rnn_long.hip",
+                                "5f3abb56d979ba104a26c69660f21374199565dcfbf10d2ec035902364c848b6"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the
