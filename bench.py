@@ -39,10 +39,10 @@ METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
     # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
-    ("C3", "mfma"): (136498.3, 270336.0, "m2rnn_mfma.hip",
-                     "97d64cc4358e5944ff6b0f11ebc2f377ad5ce89e24ab16cb684b68deb364244a"),
-    ("D1", "mfma"): (267833.6, 530989.2, "m2rnn_decode.hip",
-                     "c6d1e2c83857babaa73de8959f8e68261b4615baddae8e54cd15d2d3191123b0"),
+    ("C3", "mfma"): (136498.6, 270336.0, "m2rnn_mfma.hip",
+                     "61a0b38786d31a5bfc5785af7dd0ab18ba457c5234035cc16cffff1f6fc6d02b"),
+    ("D1", "mfma"): (267349.0, 528389.4, "m2rnn_decode.hip",
+                     "d6f09bfc7c21aa0dc4fc5e513ca60a152b47059c85446459709af8e502678a47"),
     ("C4", "mfma_long_split"): (669899.6, 1050624.0, "m2rnn_long.hip",
                                 "5f3abb56d979ba104a26c69660f21374199565dcfbf10d2ec035902364c848b6"),
     ("C5", "mfma_long_split"): (1053893.5, 2098176.0, "m2rnn_long.hip",

@@ -820,12 +820,6 @@ Plan plan_mfma(int B, int H, int K, int V, bool split) {
   return Plan{grid > 0x7fffffffLL ? -1 : (int)grid, 64 * nw, R, splits, splits > 1 ? 1 : 0, lds};
 }
 
-Plan plan_decode(int B, int H, int K, int V) {
-  const long long grid = (long long)H * decode_splits(B, H);
-  const int lds = (V * (V + 8)) * 2 + 2 * 8 * V * 4;
-  return Plan{grid > 0x7fffffffLL ? -1 : (int)grid, 256, 16, K / 16, 0, lds};
-}
-
 hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream) {
   if (!mfma_supports(a.K, a.V, a.bf16)) return hipErrorInvalidValue;
   if (decode_supports(a)) return launch_decode(a, stream);  // one step: the decoding kernel

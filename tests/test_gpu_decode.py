@@ -145,6 +145,6 @@ def test_plan_reports_the_decoding_kernel():
     from non_linear_matrix_amd import m2rnn
 
     p = m2rnn.get_plan(512, 16, 1, 128, 128, "bf16", "auto")
-    assert p["clears_y"] == 0 and p["block"] == 256 and p["grid"] == 16 * 48
+    assert p["clears_y"] == 0 and p["block"] == 256 and p["grid"] == 16 * 32
     q = m2rnn.get_plan(512, 16, 2, 128, 128, "bf16", "auto")
     assert q["grid"] == 512 * 16 * 2
