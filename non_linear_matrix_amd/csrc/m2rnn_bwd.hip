@@ -217,14 +217,15 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_bwd_kernel(BwdArgs a) {
   if (nchunks > 1) st.load(a, unit, row0, 1);
   lds_barrier();
 
-  // saved data of a step: this lane's blocks of a slot
+  // saved data of a step: this lane's blocks of a slot (read once: non-temporal)
   struct Saved {
     u4 x[KB];
   };
   auto load_slot = [&](long long off) {
     Saved r;
 #pragma unroll
-    for (int b = 0; b < KB; ++b) r.x[b] = *reinterpret_cast<const u4*>(a.saved + off + lane_off + b * 1024);
+    for (int b = 0; b < KB; ++b)
+      r.x[b] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(a.saved + off + lane_off + b * 1024));
     return r;
   };
   // state operand c H_t of step t (slot t + 1; t = -1 is H0), pre-activation c A_t.
@@ -347,8 +348,9 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_bwd_kernel(BwdArgs a) {
         const bf16x8 Bd = __builtin_bit_cast(bf16x8, pk);
         *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bd;
         {
+          // streamed out once and read once by the dW kernel: non-temporal
           char* dst = t >= 0 ? a.dA_out + (unit * T + t) * saved_slot_bytes(K, V) : a.sink;
-          *reinterpret_cast<u4*>(dst + lane_off + b * 1024) = pk;
+          __builtin_nontemporal_store(pk, reinterpret_cast<u4*>(dst + lane_off + b * 1024));
         }
 #pragma unroll
         for (int cc = 0; cc < CT; ++cc) acc[cc] = mfma(Wp[cc][b], Bd, acc[cc]);
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(256, 1) void dw_partial_kernel(const char* saved, c
   // 2 matrices x 2 row tiles x V/32 blocks x 64 lanes of 16 bytes per block
   constexpr int PIECES = 2 * 2 * (V / 32) * 64, PPT = PIECES / 256;
   static_assert(PIECES % 256 == 0, "whole pieces per thread");
-  // global reads of one block into registers
+  // global reads of one block into registers (each piece is read once: non-temporal)
   auto fetch = [&](long long blk, u4 (&x)[PPT]) {
     const int pair = static_cast<int>(blk % (rtiles / 2));  // block -> (batch row, step, row-tile pair)
     const long long bt = blk / (rtiles / 2);
@@ -437,7 +439,8 @@ __global__ __launch_bounds__(256, 1) void dw_partial_kernel(const char* saved, c
     for (int r = 0; r < PPT; ++r) {
       const int p = tid + 256 * r;
       const int m = p / (2 * (V / 32) * 64), q = p % (2 * (V / 32) * 64);
-      x[r] = *reinterpret_cast<const u4*>(srcs[m] + (long long)(2 * pair) * (V / 32) * 1024 + q * 16);
+      x[r] = __builtin_nontemporal_load(
+          reinterpret_cast<const u4*>(srcs[m] + (long long)(2 * pair) * (V / 32) * 1024 + q * 16));
     }
   };
   // the same pieces, row-major into LDS

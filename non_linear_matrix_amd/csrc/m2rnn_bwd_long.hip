@@ -217,16 +217,18 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
   // t + 1, H0 for t = -1) and the pre-activation c A_t, this lane's 16 bytes.
   // Inert steps (t < 0) read a clamped step: any finite data does, since their
   // gate 1 zeroes dA and their dy, v, q are zero. The loads carry no branch, so
-  // the waits for them count exactly the operations issued after them.
+  // the waits for them count exactly the operations issued after them. Each
+  // saved piece is read once: non-temporal loads.
   auto load_state = [&](long long i) {
     const long long t = (long long)T - 1 - i;
     const int slot = static_cast<int>(t + 1 < 0 ? 0 : t + 1);
-    return *reinterpret_cast<const u4*>(a.saved + saved_state_off(unit, slot, T, K, V) + lane_off);
+    return __builtin_nontemporal_load(reinterpret_cast<const u4*>(a.saved + saved_state_off(unit, slot, T, K, V) + lane_off));
   };
   auto load_pre = [&](long long i) {
     const long long t = (long long)T - 1 - i;
     const int tc = static_cast<int>(t < 0 ? 0 : t);
-    return *reinterpret_cast<const u4*>(a.saved + saved_pre_off(unit, tc, a.B, a.H, T, K, V) + lane_off);
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const u4*>(a.saved + saved_pre_off(unit, tc, a.B, a.H, T, K, V) + lane_off));
   };
   // rings indexed by step index mod kRing: state i is read at steps i and i - 1,
   // the pre-activation at step i
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(BwdLongLayout<V>::THREADS, 1) void mfma_bwd_long_ke
         rs[((S + w) * kChunk + s) * 64 + l] = dkp;
         dfs[(w * kChunk + s) * 64 + l] = row_sum16(dfp);
         char* dst = t >= 0 ? a.dA_out + (unit * T + t) * saved_slot_bytes(K, V) : a.dA_sink;
-        *reinterpret_cast<u4*>(dst + lane_off) = pk;
+        __builtin_nontemporal_store(pk, reinterpret_cast<u4*>(dst + lane_off));  // read once, by the dW kernel
       }
       if constexpr (s + 1 < kChunk) pre = precompute(s + 1);
       // dv: read out the step pair (s - 1, s) on this wave's columns
