@@ -156,7 +156,12 @@ def test_deterministic(algo):
 @pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split", "mfma_long", "mfma_long_split"])
 def test_chunked_continuation(algo):
     """fwd(T1) then fwd(T2, H0 = H_T) continues fwd(T1 + T2): bitwise for the fp32
-    kernel, within the bf16 bar for the matrix-core kernel."""
+    kernel. The matrix-core kernels carry c H (c = 2 / ln 2) and hand back
+    H_T = (c H) / c in fp32, so the continued call can start one rounding away
+    from the single call's state: with the split operand that stays at the fp32
+    level (bound 5e-5; measured ~2e-6 to 4e-6), with one bf16 operand a one-ulp
+    change can move one element's operand rounding (2^-9) and carry it forward
+    (bound 2^-8; measured 4e-8 to 3e-4)."""
     import torch
     from non_linear_matrix_amd import m2rnn
     cfg = scaled(CONFIGS["C3"], B=2, H=2, T=50)
@@ -174,14 +179,19 @@ def test_chunked_continuation(algo):
     if algo == "simple":
         assert torch.equal(yc, y) and torch.equal(HTb, HT)
     else:
-        assert nerr(yc.cpu().numpy(), y.cpu().numpy().astype(np.float64)) <= 1e-2
-        assert nerr(HTb.cpu().numpy(), HT.cpu().numpy().astype(np.float64)) <= 1e-2
+        ey = nerr(yc.cpu().numpy(), y.cpu().numpy().astype(np.float64))
+        eh = nerr(HTb.cpu().numpy(), HT.cpu().numpy().astype(np.float64))
+        print(f"{algo}: continuation against one call: y {ey:.2e} H_T {eh:.2e}", flush=True)
+        tol = 5e-5 if algo.endswith("split") else 2.0 ** -8
+        assert ey <= tol and eh <= tol
 
 
 @pytest.mark.parametrize("algo", ["mfma", "mfma_split", "mfma_long", "mfma_long_split"])
 def test_readout_self_consistency(algo):
-    """y_T against H_T^T q_T recomputed in fp64 from the kernel's own H_T (the
-    readout uses the state rounded to bf16 as a matrix operand)."""
+    """y_T against H_T^T q_T recomputed in fp64 from the kernel's own H_T. The
+    single-operand families read out from the state rounded to bf16 (2^-9
+    relative per element; bound 8e-3, measured 2.2e-3); the split families from
+    both bf16 halves, ~16 significant bits (bound 1e-4, measured 2e-6 to 4e-6)."""
     from non_linear_matrix_amd.inputs import bf16_bits_to_fp32
     cfg = scaled(CONFIGS["C3"], B=2, H=4, T=20)
     x = generate(cfg, 9)
@@ -189,7 +199,9 @@ def test_readout_self_consistency(algo):
     y, HT = gpu_run(x, algo=algo)
     q = bf16_bits_to_fp32(x["q"]).astype(np.float64)
     yT = np.einsum("bhkv,bhk->bhv", HT.astype(np.float64), q[:, :, -1])
-    assert nerr(y[:, :, -1], yT) <= 8e-3
+    e = nerr(y[:, :, -1], yT)
+    print(f"{algo}: y_T against H_T^T q_T {e:.2e}", flush=True)
+    assert e <= (1e-4 if algo.endswith("split") else 8e-3)
 
 
 def test_nondefault_stream_ordering():
