@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
+SPLIT_GUARD = 1e-3
 
 
 def _tol(cfg, algo):
@@ -56,6 +57,11 @@ def test_full_size_configs(name, algo):
     tol = _tol(CONFIGS[name], algo)
     ey, eh = full_parity(name, algo, tol)
     assert ey <= tol and eh <= tol
+    if algo.endswith("split"):
+        # the split operand carries ~16 significant bits: measured at most 1.1e-4
+        # (C2, H_T) on these workloads, so 1e-3 catches a lost low half long
+        # before the 2e-2 bar would
+        assert ey <= SPLIT_GUARD and eh <= SPLIT_GUARD
 
 
 # The single bf16 operand (MFMA, MFMA_LONG) meets the bar on C3 and C4, but on C2
