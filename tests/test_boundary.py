@@ -167,6 +167,20 @@ def test_auto_picks_a_kernel_that_covers_the_shape():
     assert p["algo"] == "mfma_long_split" and p["grid"] == 256 and p["block"] == 256 and p["clears_y"] == 1
 
 
+def test_decoding_plan():
+    """Every T = 1 call on the matrix-core shapes plans the one-step kernel: 256
+    threads, two workgroups per CU by LDS (at most 80 KiB each), about 512
+    workgroups spread over the heads with at least one batch row each. Host only."""
+    p = m2rnn.get_plan(512, 16, 1, 128, 128, "bf16", "auto")
+    assert p["block"] == 256 and p["grid"] == 16 * 32 and p["clears_y"] == 0
+    assert 0 < p["lds_bytes"] <= 80 * 1024
+    for K, V in [(32, 64), (64, 64), (128, 64), (32, 128), (64, 128)]:
+        q = m2rnn.get_plan(3, 5, 1, K, V, "bf16", "mfma_split")
+        assert q["grid"] == 5 * 3 and q["block"] == 256, (K, V)   # min(B, ceil(512 / H)) rows per head
+        assert 0 < q["lds_bytes"] <= 80 * 1024, (K, V)
+    assert m2rnn.get_plan(1000, 1, 1, 128, 128, "bf16", "auto")["grid"] == 512
+
+
 def test_deterministic_flag_and_the_long_kernels():
     """M2RNN_FLAG_DETERMINISTIC: the long kernels round each row tile's readout
     onto a common grid, so their y is repeatable onto the y the call clears (any
