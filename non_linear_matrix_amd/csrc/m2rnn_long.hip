@@ -57,14 +57,20 @@ struct LongLayout {
   static constexpr int CT = V / 16;       // 16-column tiles
   static constexpr int THREADS = 64 * S;
   static constexpr int HROW = V + 8;      // bf16 per state-tile row (padded)
-  static constexpr int NVX = 2 * CT + 4;  // dwords per (step, column-in-tile) of rank-1 A records
-  static constexpr int NHS = 4;           // state-tile slots (the readout lags a step)
+  // dwords per (step, column-in-tile) of rank-1 A records: one (v, v) pair per
+  // column tile, padded by two so that the 16 rows a 16-lane group reads fall
+  // on distinct banks
+  static constexpr int NVX = CT + 2;
+  // state-tile slots, for the high and for the low halves: the readout of the
+  // step pair (s - 1, s) runs after step s's barrier, and the next write into
+  // step s - 1's slot, at step s + 3, comes two barriers later
+  static constexpr int NHS = 4;
   static constexpr int KX_BYTES = 2 * kChunk * 16 * 4;
   static constexpr int QS_BYTES = 2 * kChunk * 16 * 2;
   static constexpr int FS_BYTES = 2 * kChunk * 4 * 4;
   static constexpr int VX_BYTES = 2 * kChunk * 16 * NVX * 4;
   static constexpr int XB_BYTES = NHS * 16 * HROW * 2;
-  static constexpr int XL_BYTES = 2 * 16 * HROW * 2;
+  static constexpr int XL_BYTES = NHS * 16 * HROW * 2;
   static constexpr int KX_OFF = 0;
   static constexpr int QS_OFF = KX_OFF + KX_BYTES;
   static constexpr int FS_OFF = QS_OFF + QS_BYTES;
@@ -82,7 +88,8 @@ struct LongLayout {
   static constexpr int YB_OFF = YS_OFF + YS_BYTES;
   static constexpr int Z_OFF = YB_OFF + YB_BYTES;
   static constexpr int TOTAL = Z_OFF + 16;
-  static_assert(V * HROW * 2 <= VX_BYTES, "W fits in the rank-1 region during the prologue");
+  static_assert(V * HROW * 2 <= VX_BYTES + XB_BYTES + XL_BYTES,
+                "W fits in the rank-1 and state-tile regions during the prologue");
   static_assert(2 * TOTAL <= 160 * 1024, "two workgroups per CU");
   // 16-byte global pieces of one chunk: k of the tile's 16 rows, q of them
   // (without GRID), v
@@ -216,7 +223,7 @@ struct LongStager {
           const int col = 8 * part + i;
           const unsigned int raw = (r[i / 2] >> (16 * (i % 2))) & 0xffffu;
           const int tile = col / 16;
-          vx[(s * 16 + col % 16) * L::NVX + 4 * (tile / 2) + tile % 2] = raw | (raw << 16);
+          vx[(s * 16 + col % 16) * L::NVX + tile] = raw | (raw << 16);
         }
       }
     }
@@ -300,10 +307,6 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
     for (int j = 0; j < 2; ++j)
       G[j] = H0 ? *reinterpret_cast<const f4*>(H0 + 16 * (2 * w + j) + 4 * g) * kC : f4{0, 0, 0, 0};
   }
-  // zeroed state-tile slots: the readout of an odd final step multiplies a slot
-  // that step never wrote (by zero q), which must not hold NaN patterns
-  for (int i = tid; i < (L::XB_BYTES + L::XL_BYTES) / 4; i += L::THREADS)
-    reinterpret_cast<unsigned int*>(lds + L::XB_OFF)[i] = 0u;
   // W^T fragments of this wave's two output tiles, every contraction block, via
   // LDS. Register arrays over the blocks are indexed o = 0 .. KB - 1 for block
   // (w + o) mod KB (o = 0: the wave's own block), so that every register index
@@ -331,14 +334,13 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
         asm volatile("" : "=a"(wa) : "0"(wa));
         Wf[j][o] = __builtin_bit_cast(bf16x8, wa);
       }
-    lds_barrier();  // the region is the rank-1 stage buffers from here on
+    lds_barrier();  // the regions are the rank-1 stage buffers and state tiles from here on
   }
-  // LDS init: the zero dwords of the rank-1 records, the zero word; chunks 0, 1
-  for (int i = tid; i < 2 * kChunk * 16; i += L::THREADS)
-#pragma unroll
-    for (int k = 0; k < L::CT / 2; ++k)
-      *reinterpret_cast<uint2*>(reinterpret_cast<unsigned int*>(lds + L::VX_OFF) + i * L::NVX + 4 * k + 2) =
-          uint2{0u, 0u};
+  // zeroed state-tile slots: the readout of an odd final step multiplies a slot
+  // that step never wrote (by zero q), which must not hold NaN patterns
+  for (int i = tid; i < (L::XB_BYTES + L::XL_BYTES) / 4; i += L::THREADS)
+    reinterpret_cast<unsigned int*>(lds + L::XB_OFF)[i] = 0u;
+  // LDS init: the zero word; chunks 0, 1
   if (tid < 4) reinterpret_cast<unsigned int*>(lds + L::Z_OFF)[tid] = 0u;
   // the y grid's state bound: after the last staged chunk (wave 0), and per step
   // of that chunk (lanes 0 .. 15)
@@ -367,16 +369,16 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
     }
   };
   // the shared state tile slot of step s: row n, block b at columns 32 b + 8 g
-  auto publish_own = [&](int slot, int lslot) {
+  auto publish_own = [&](int slot) {
     *reinterpret_cast<bf16x8*>(xb + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bf[0];
-    if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(xl + lslot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bl[0];
+    if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(xl + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bl[0];
   };
-  auto fetch_others = [&](int slot, int lslot) {
+  auto fetch_others = [&](int slot) {
 #pragma unroll
     for (int o = 1; o < KB; ++o) {
       const int b = (w + o) % KB;
       Bf[o] = *reinterpret_cast<const bf16x8*>(xb + slot * 16 * HROW + n * HROW + 32 * b + 8 * g);
-      if constexpr (SPLIT) Bl[o] = *reinterpret_cast<const bf16x8*>(xl + lslot * 16 * HROW + n * HROW + 32 * b + 8 * g);
+      if constexpr (SPLIT) Bl[o] = *reinterpret_cast<const bf16x8*>(xl + slot * 16 * HROW + n * HROW + 32 * b + 8 * g);
     }
   };
   // rank-1 term of step s of the chunk in stage buffer sb: acc[j] = (v, tile 2w + j) x (hi, lo of c k)
@@ -384,14 +386,14 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
     const unsigned int* kx = kx_all + sb * kChunk * 16;
     const unsigned int* vx = vx_all + sb * kChunk * 16 * L::NVX;
     const unsigned int kp = *((g == 0) ? kx + s * 16 + n : zero_lds);
-    // 16x16x32: A the record (v pairs of tiles 2w, 2w + 1, then its two zero
-    // dwords), B the (hi, lo) pair of c k in the slots of the tile. Not the
+    // 16x16x32: A the (v, v) pairs of tiles 2w, 2w + 1 and zeros, B the (hi, lo)
+    // pair of c k in the slots of the tile. Not the
     // 16x16x16 form: on gfx950 a 16x16x32 product that took a 16x16x16 result as
     // its accumulator a few instructions later read it before the result was
     // there, and here the compiler places the rank-1 write within a few
     // instructions of the first product into the same accumulator.
-    const u4 win = *reinterpret_cast<const u4*>(vx + (s * 16 + n) * L::NVX + 4 * w);
-    const bf16x8 av = __builtin_bit_cast(bf16x8, win);
+    const uint2 win = *reinterpret_cast<const uint2*>(vx + (s * 16 + n) * L::NVX + 2 * w);
+    const bf16x8 av = __builtin_bit_cast(bf16x8, u4{win.x, win.y, 0u, 0u});
     acc[0] = mfma(av, __builtin_bit_cast(bf16x8, u4{kp, 0u, 0u, 0u}), f4{0, 0, 0, 0});
     acc[1] = mfma(av, __builtin_bit_cast(bf16x8, u4{0u, kp, 0u, 0u}), f4{0, 0, 0, 0});
   };
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
           (__attribute__((address_space(3))) s4*)(src + 16 * P + 4 * HROW));
       r.s[j] = __builtin_bit_cast(bf16x8, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       if constexpr (SPLIT) {
-        const unsigned short* srl = xl + (s & 1) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
+        const unsigned short* srl = xl + (s & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
         const s4 llo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(srl + 16 * P));
         const s4 lhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s4*)(srl + 16 * P + 4 * HROW));
@@ -498,9 +500,9 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   // initial operand: every wave's block of G_0 through the shared tile (slot NHS - 1)
   make_own();
   if constexpr (SAVE) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, 0, T, a.K, V) + sv_off) = Bf[0];
-  publish_own(NHS - 1, 1);
+  publish_own(NHS - 1);
   lds_barrier();  // staged chunks, W-region reuse, and the operand blocks are visible
-  fetch_others(NHS - 1, 1);
+  fetch_others(NHS - 1);
   f4 acc[2];
   f4 gate = *reinterpret_cast<const f4*>(fs_all);  // step 0's gate scalars
   if (nchunks > 0) {
@@ -546,13 +548,13 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
       if constexpr (SAVE) {
         if (t < Tb) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, t + 1, T, a.K, V) + sv_off) = Bf[0];
       }
-      publish_own(s & (NHS - 1), s & 1);
+      publish_own(s & (NHS - 1));
       products(0, accn);
       lds_barrier();
       gate = *reinterpret_cast<const f4*>((s + 1 < kChunk ? fsb : fsn) + 4 * ((s + 1) % kChunk));
       ReadoutOps ro;
       if constexpr ((s & 1) != 0) ro = readout_load(sb, s - 1, 2);
-      fetch_others(s & (NHS - 1), s & 1);
+      fetch_others(s & (NHS - 1));
       // tile by tile: tile 0's sum is complete while tile 1's last KB - 1
       // blocks (twice as many MFMAs when split) still run, and the next step's
       // epilogue of tile 0 issues under them
