@@ -43,10 +43,10 @@ TRAFFIC_KIB = {
                      "61a0b38786d31a5bfc5785af7dd0ab18ba457c5234035cc16cffff1f6fc6d02b"),
     ("D1", "mfma"): (267349.0, 528389.4, "m2rnn_decode.hip",
                      "d6f09bfc7c21aa0dc4fc5e513ca60a152b47059c85446459709af8e502678a47"),
-    ("C4", "mfma_long_split"): (669899.6, 1050624.0, "m2rnn_long.hip",
-                                "5f3abb56d979ba104a26c69660f21374199565dcfbf10d2ec035902364c848b6"),
-    ("C5", "mfma_long_split"): (1053893.5, 2098176.0, "m2rnn_long.hip",
-                                "5f3abb56d979ba104a26c69660f21374199565dcfbf10d2ec035902364c848b6"),
+    ("C4", "mfma_long_split"): (669893.3, 1050624.0, "m2rnn_long.hip",
+                                "efcf06bc279dd92f541895dcbec5a34b5a7d1b3424b485541ca93b8934495259"),
+    ("C5", "mfma_long_split"): (1053893.0, 2098176.0, "m2rnn_long.hip",
+                                "efcf06bc279dd92f541895dcbec5a34b5a7d1b3424b485541ca93b8934495259"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the
