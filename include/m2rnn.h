@@ -93,11 +93,16 @@ typedef enum m2rnn_dtype {
  *             fp64 definition on every workload measured).
  * AUTO:       fp32: MFMA_F32. bf16 with V in {64, 128}, T > 1 and at most
  *             768 16-row tiles (B H K / 16 <= 768; two workgroups fit per CU of
- *             a 256-CU gfx950): MFMA_LONG_SPLIT; else MFMA_SPLIT where it covers
- *             the shape, else SIMPLE. Every choice gives a bitwise repeatable y
- *             onto a y the call clears; with M2RNN_FLAG_DETERMINISTIC and
- *             M2RNN_FLAG_ACCUMULATE_Y together it avoids the families that add
- *             two or more partial readouts into y.
+ *             a 256-CU gfx950): MFMA_LONG_F16; else MFMA_F16 where it covers
+ *             the shape, else SIMPLE. The fp16 operand meets the 2e-2 bar on
+ *             every unit of every workload measured, at the single operand's
+ *             cost; inputs outside its domain (see MFMA_F16) need MFMA_SPLIT or
+ *             MFMA_LONG_SPLIT, named explicitly. Every choice gives a bitwise
+ *             repeatable y onto a y the call clears; with
+ *             M2RNN_FLAG_DETERMINISTIC and M2RNN_FLAG_ACCUMULATE_Y together it
+ *             avoids the families that add two or more partial readouts into y.
+ *             The training entry points resolve AUTO to MFMA_SPLIT or
+ *             MFMA_LONG_SPLIT (the backward pass reads bf16 operands).
  * MFMA_LONG, MFMA_LONG_SPLIT: the same arithmetic as MFMA / MFMA_SPLIT, for
  *             workloads with few 16-row tiles (B H K / 16 well below the GPU's
  *             1024 SIMDs: small batches, long sequences). Each tile's V columns
@@ -118,7 +123,23 @@ typedef enum m2rnn_dtype {
  *             the backward pass covers) and write the same `saved` layout.
  *             MFMA_LONG has MFMA's precision (misses the bar on the same two
  *             workloads: H_T 2.6e-2, y 2.6e-2); MFMA_LONG_SPLIT has MFMA_SPLIT's
- *             (both halves in the products and the readout). */
+ *             (both halves in the products and the readout).
+ * MFMA_F16, MFMA_LONG_F16: MFMA / MFMA_LONG with the state operand rounded to
+ *             fp16 (round-to-nearest-even, 11 significant bits: 2^-12 relative
+ *             per step instead of 2^-9) on v_mfma_f32_16x16x32_f16, at the single
+ *             operand's cost; W and q are converted from bf16 to fp16 inside the
+ *             kernel (exact for magnitudes in [2^-17, 65504]). Their domain is
+ *             fp16's range: |W| and |q| at most 65504, max |H0| at most 22 700
+ *             (the operand is 2/ln 2 H, and |H_t| <= max(1, max |H0|) for gates
+ *             in [0, 1]); a W, q or H0 value beyond it makes the outputs it
+ *             reaches NaN (never a finite wrong value), and gates outside [0, 1]
+ *             are outside the method. Magnitudes below fp16's normal range
+ *             (6.1e-5) keep fewer bits (absolute rounding 2^-25), which matters
+ *             only for workloads whose states and inputs are all that small.
+ *             Forward only (no training entry point takes them); one step
+ *             (T = 1) runs the decoding kernel as for every matrix-core family;
+ *             their y is as repeatable as MFMA's / MFMA_LONG's. Measured on
+ *             every unit of the five workloads: see the parity tests. */
 typedef enum m2rnn_algo {
   M2RNN_ALGO_AUTO = 0,
   M2RNN_ALGO_SIMPLE = 1,
@@ -126,7 +147,9 @@ typedef enum m2rnn_algo {
   M2RNN_ALGO_MFMA_SPLIT = 3,
   M2RNN_ALGO_MFMA_LONG = 4,
   M2RNN_ALGO_MFMA_LONG_SPLIT = 5,
-  M2RNN_ALGO_MFMA_F32 = 6
+  M2RNN_ALGO_MFMA_F32 = 6,
+  M2RNN_ALGO_MFMA_F16 = 7,
+  M2RNN_ALGO_MFMA_LONG_F16 = 8
 } m2rnn_algo;
 
 /* The forward recurrence with the automatically chosen kernel. */
@@ -373,7 +396,7 @@ const char* m2rnn_status_string(m2rnn_status status);
  * choice of MFMA_LONG_SPLIT and M2RNN_FLAG_DETERMINISTIC, 0.6.0 MFMA_LONG* in
  * the training forwards and m2rnn_bwd_algo, 0.7.0 m2rnn_get_plan_ex and
  * m2rnn_bwd_noalloc, 0.8.0 MFMA_F32, 0.9.0 the grid-rounded, order-independent y of
- * MFMA_LONG*). */
+ * MFMA_LONG*, 0.10.0 MFMA_F16 and MFMA_LONG_F16). */
 int m2rnn_version(void);
 
 #ifdef __cplusplus

@@ -39,10 +39,12 @@ m2rnn_status check(const void* k, const void* v, const void* q, const void* f, c
       return M2RNN_SUCCESS;
     case M2RNN_ALGO_MFMA:
     case M2RNN_ALGO_MFMA_SPLIT:
+    case M2RNN_ALGO_MFMA_F16:
       return m2rnn::mfma_supports(K, V, dt == M2RNN_DTYPE_BF16) ? M2RNN_SUCCESS
                                                                  : M2RNN_ERROR_NOT_SUPPORTED;
     case M2RNN_ALGO_MFMA_LONG:
     case M2RNN_ALGO_MFMA_LONG_SPLIT:
+    case M2RNN_ALGO_MFMA_LONG_F16:
       return (dt == M2RNN_DTYPE_BF16 && (V == 64 || V == 128)) ? M2RNN_SUCCESS : M2RNN_ERROR_NOT_SUPPORTED;
     case M2RNN_ALGO_MFMA_F32:
       return (dt == M2RNN_DTYPE_F32 && m2rnn::mfma_f32_supports(K, V)) ? M2RNN_SUCCESS : M2RNN_ERROR_NOT_SUPPORTED;
@@ -57,13 +59,14 @@ extern "C" m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_d
 
 namespace {
 
-// The training entry points' forward kernel: AUTO takes the split operand, on
-// the latency-oriented kernel where m2rnn_pick_algo would; explicit families
-// are the four matrix-core ones, on the shapes the backward pass covers.
+// The training entry points' forward kernel: AUTO takes the split operand (the
+// backward pass reads bf16 operands), on the latency-oriented kernel where
+// m2rnn_pick_algo would; explicit families are the four bf16 matrix-core ones,
+// on the shapes the backward pass covers.
 m2rnn_status training_algo(m2rnn_algo& algo, int B, int H, int T, int K, int V, m2rnn_dtype dt) {
   if (algo == M2RNN_ALGO_AUTO) {
     algo = m2rnn_pick_algo(B, H, T, K, V, dt);
-    if (algo != M2RNN_ALGO_MFMA_LONG_SPLIT) algo = M2RNN_ALGO_MFMA_SPLIT;
+    algo = algo == M2RNN_ALGO_MFMA_LONG_F16 ? M2RNN_ALGO_MFMA_LONG_SPLIT : M2RNN_ALGO_MFMA_SPLIT;
   }
   switch (algo) {
     case M2RNN_ALGO_MFMA:
@@ -77,8 +80,17 @@ m2rnn_status training_algo(m2rnn_algo& algo, int B, int H, int T, int K, int V, 
   }
 }
 
-bool is_long(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT; }
+bool is_long(m2rnn_algo algo) {
+  return algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT || algo == M2RNN_ALGO_MFMA_LONG_F16;
+}
 bool is_split(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_SPLIT || algo == M2RNN_ALGO_MFMA_LONG_SPLIT; }
+bool is_f16(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_F16 || algo == M2RNN_ALGO_MFMA_LONG_F16; }
+// the multi-step kernel family with a latency-oriented family's state operand
+m2rnn_algo multistep_of(m2rnn_algo algo) {
+  return algo == M2RNN_ALGO_MFMA_LONG ? M2RNN_ALGO_MFMA
+         : algo == M2RNN_ALGO_MFMA_LONG_F16 ? M2RNN_ALGO_MFMA_F16
+                                            : M2RNN_ALGO_MFMA_SPLIT;
+}
 
 // Whether a forward call's y is bitwise repeatable (the order of its atomic adds
 // cannot change it). Kernels whose workgroups share a unit add their readouts
@@ -93,7 +105,8 @@ bool is_split(m2rnn_algo algo) { return algo == M2RNN_ALGO_MFMA_SPLIT || algo ==
 bool atomic_free(m2rnn_algo algo, int T, int K, int V, bool bf16, bool accumulate) {
   int adds = 1;
   const bool decode = T == 1 && m2rnn::mfma_supports(K, V, bf16);
-  if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT) adds = decode ? 1 : m2rnn::mfma_groups(K);
+  if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT || algo == M2RNN_ALGO_MFMA_F16)
+    adds = decode ? 1 : m2rnn::mfma_groups(K);
   if (is_long(algo)) adds = decode ? 1 : K / 16;
   return adds <= 1 || (!accumulate && (adds == 2 || is_long(algo)));
 }
@@ -110,9 +123,7 @@ m2rnn_status resolve_algo(m2rnn_algo& algo, int B, int H, int T, int K, int V, m
   if (algo == M2RNN_ALGO_AUTO) {
     algo = m2rnn_pick_algo(B, H, T, K, V, dt);
     if (det && !atomic_free(algo, T, K, V, bf, acc) && is_long(algo))
-      algo = !m2rnn::mfma_supports(K, V, bf) ? M2RNN_ALGO_SIMPLE
-             : algo == M2RNN_ALGO_MFMA_LONG  ? M2RNN_ALGO_MFMA
-                                             : M2RNN_ALGO_MFMA_SPLIT;
+      algo = !m2rnn::mfma_supports(K, V, bf) ? M2RNN_ALGO_SIMPLE : multistep_of(algo);
     if (det && !atomic_free(algo, T, K, V, bf, acc)) algo = M2RNN_ALGO_SIMPLE;
   }
   if (det && !atomic_free(algo, T, K, V, bf, acc)) return M2RNN_ERROR_NOT_SUPPORTED;
@@ -137,11 +148,14 @@ m2rnn_algo m2rnn_pick_algo(int B, int H, int T, int K, int V, m2rnn_dtype in_dty
   // multi-step kernel (one wave per tile, 1024 at once); beyond that the latter
   // wins (measured at K = V = 128).
   constexpr long double kLongMaxTiles = 768;
+  // bf16 inputs: the fp16 state operand, which meets the bf16 bar on every
+  // workload measured at the single operand's cost (the split operand costs a
+  // third more time; it stays the choice of the training entry points)
   if (in_dtype == M2RNN_DTYPE_F32 && m2rnn::mfma_f32_supports(K, V)) return M2RNN_ALGO_MFMA_F32;
   if (in_dtype == M2RNN_DTYPE_BF16 && T > 1 && (V == 64 || V == 128) && supported_dim(K) &&
       (long double)B * H * (K / 16) <= kLongMaxTiles)
-    return M2RNN_ALGO_MFMA_LONG_SPLIT;
-  if (m2rnn::mfma_supports(K, V, in_dtype == M2RNN_DTYPE_BF16)) return M2RNN_ALGO_MFMA_SPLIT;
+    return M2RNN_ALGO_MFMA_LONG_F16;
+  if (m2rnn::mfma_supports(K, V, in_dtype == M2RNN_DTYPE_BF16)) return M2RNN_ALGO_MFMA_F16;
   return M2RNN_ALGO_SIMPLE;
 }
 
@@ -157,11 +171,11 @@ m2rnn_status m2rnn_fwd_varlen(const void* k, const void* v, const void* q, const
                    (flags & M2RNN_FLAG_ACCUMULATE_Y) ? 1 : 0, seq_len, nullptr};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT)
-    e = m2rnn::launch_mfma(a, algo == M2RNN_ALGO_MFMA_SPLIT, s);
-  else if (algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT)
+  if (algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT || algo == M2RNN_ALGO_MFMA_F16)
+    e = m2rnn::launch_mfma(a, algo == M2RNN_ALGO_MFMA_SPLIT, s, is_f16(algo));
+  else if (is_long(algo))
     e = m2rnn::decode_supports(a) ? m2rnn::launch_decode(a, s)  // one step: the decoding kernel
-                                  : m2rnn::launch_long(a, algo == M2RNN_ALGO_MFMA_LONG_SPLIT, s);
+                                  : m2rnn::launch_long(a, algo == M2RNN_ALGO_MFMA_LONG_SPLIT, s, is_f16(algo));
   else if (algo == M2RNN_ALGO_MFMA_F32)
     e = m2rnn::launch_mfma_f32(a, s);
   else
@@ -369,8 +383,8 @@ m2rnn_status m2rnn_get_plan_ex(int B, int H, int T, int K, int V, m2rnn_dtype in
   m2rnn_status st = check(p, p, p, p, p, nullptr, pf, nullptr, B, H, T, K, V, in_dtype, algo);
   if (st != M2RNN_SUCCESS) return st;
   if ((st = resolve_algo(algo, B, H, T, K, V, in_dtype, flags)) != M2RNN_SUCCESS) return st;
-  const bool mf = algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT;
-  const bool lg = algo == M2RNN_ALGO_MFMA_LONG || algo == M2RNN_ALGO_MFMA_LONG_SPLIT;
+  const bool mf = algo == M2RNN_ALGO_MFMA || algo == M2RNN_ALGO_MFMA_SPLIT || algo == M2RNN_ALGO_MFMA_F16;
+  const bool lg = is_long(algo);
   m2rnn::Plan pl = algo == M2RNN_ALGO_MFMA_F32 ? m2rnn::plan_mfma_f32(B, H, K, V)
                    : !(mf || lg)                 ? m2rnn::plan_simple(B, H, K, V)
                    : T == 1 && m2rnn::mfma_supports(K, V, 1) ? m2rnn::plan_decode(B, H, K, V)
@@ -411,6 +425,6 @@ const char* m2rnn_status_string(m2rnn_status status) {
   }
 }
 
-int m2rnn_version(void) { return 900; }
+int m2rnn_version(void) { return 1000; }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
 // Device helpers shared by the kernel files: vector types, bf16 <-> fp32
-// conversions, the 16x16x32 bf16 matrix product, the LDS-only workgroup barrier,
+// conversions, the 16x16x32 bf16 and fp16 matrix products, the LDS-only workgroup barrier,
 // a 16-lane DPP row sum and a compile-time loop. Included by the .hip sources only.
 #pragma once
 
@@ -13,6 +13,7 @@ namespace dev {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) float f2;
 typedef __attribute__((ext_vector_type(4))) float f4;
 typedef __attribute__((ext_vector_type(8))) float f8;
@@ -40,6 +41,28 @@ __device__ __forceinline__ unsigned int pack_bf16(float x0, float x1) {
 // D = A B + C on a 16x16 fp32 tile, A and B bf16 with 32-deep contraction
 __device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// the same product with fp16 operands (11 significant bits instead of 8)
+__device__ __forceinline__ f4 mfma(const f16x8& a, const f16x8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// Largest magnitude an fp16 operand takes: beyond it the kernels put NaN in the
+// operand (rather than the infinity the conversion would give, which tanh could
+// turn into a finite, wrong state), so a value outside fp16's range shows as NaN
+// in the outputs.
+constexpr float kF16Max = 65504.0f;
+__device__ __forceinline__ float f16_range_or_nan(float x) {
+  return fabsf(x) <= kF16Max ? x : __builtin_nanf("");
+}
+// eight bf16 bit patterns to fp16, round to nearest even: exact for magnitudes
+// from 2^-17 to 65504 (a bf16 significand has 8 bits, fp16 keeps 11 and its
+// subnormals reach 2^-24); larger magnitudes give NaN
+__device__ __forceinline__ f16x8 bf16x8_to_f16(const s8& b) {
+  f8 x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = f16_range_or_nan(bf16_to_f32(static_cast<unsigned short>(b[i])));
+  return __builtin_convertvector(x, f16x8);
 }
 
 // Workgroup barrier that orders LDS only: global loads and atomics stay in

@@ -49,8 +49,9 @@ __host__ __device__ inline long long saved_total_bytes(int B, int H, int T, int 
 hipError_t launch_simple(const FwdArgs& a, hipStream_t stream);
 // Returns hipErrorInvalidValue when the MFMA kernel does not cover the shape
 // (callers check mfma_supports first).
-// split: state operand as bf16 hi + lo (two MFMA passes) instead of one bf16.
-hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream);
+// split: state operand as bf16 hi + lo (two MFMA passes) instead of one bf16;
+// f16: one fp16 state operand (W and q converted to fp16; no saved data).
+hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream, bool f16 = false);
 bool mfma_supports(int K, int V, int bf16);
 // fp32 matrix-core kernel (m2rnn_f32.hip): fp32 inputs, no saved data; writes y
 // itself in a fixed summation order (clears it only for ragged lengths).
@@ -125,6 +126,6 @@ Plan plan_mfma_f32(int B, int H, int K, int V);
 // 16-row tile; y summed over the tiles with atomic adds.
 bool long_supports(const FwdArgs& a);
 Plan plan_long(int B, int H, int K, int V);
-hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream);
+hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream, bool f16 = false);
 
 }  // namespace m2rnn

@@ -117,9 +117,15 @@ __device__ __forceinline__ float row_prod16(float x) {
 
 // One chunk of per-step inputs for the tile's 16 rows: loaded to registers, then
 // stored into a stage buffer in the forms the MFMAs read.
-template <int V, bool GRID>
+// F16: q is staged as fp16 (the readout's operand type)
+template <int V, bool GRID, bool F16 = false>
 struct LongStager {
   using L = LongLayout<V, GRID>;
+  // 8 staged q values (bf16 bit patterns) as stored in LDS
+  static __device__ __forceinline__ u4 q_out(const u4& r) {
+    if constexpr (F16) return __builtin_bit_cast(u4, bf16x8_to_f16(__builtin_bit_cast(s8, r)));
+    return r;
+  }
   u4 reg[L::PPT];
   u4 qreg[L::QPT > 0 ? L::QPT : 1];
   unsigned short freg;
@@ -180,7 +186,7 @@ struct LongStager {
       qa = row_sum16(qa);
       if (i % 16 == 0) yb[st] = qa;
       // the tile's own rows are the readout's q
-      if (own == 0 || own == 1) *reinterpret_cast<u4*>(qsg + st * 16 + 8 * own) = qreg[j];
+      if (own == 0 || own == 1) *reinterpret_cast<u4*>(qsg + st * 16 + 8 * own) = q_out(qreg[j]);
     }
     if (tid < 64) {
       // M_t - 1 = f_t (M_{t-1} - 1) and M >= 1, so M is non-increasing: the bound
@@ -214,7 +220,7 @@ struct LongStager {
         }
       } else if (slot < L::P_K + L::P_Q) {
         const int s2 = slot - L::P_K, s = s2 / 2, part = s2 % 2;
-        *reinterpret_cast<u4*>(qs + s * 16 + 8 * part) = r;
+        *reinterpret_cast<u4*>(qs + s * 16 + 8 * part) = q_out(r);
       } else if (slot < L::PIECES) {
         const int s2 = slot - L::P_K - L::P_Q;
         const int s = s2 / (V / 8), part = s2 % (V / 8);
@@ -238,9 +244,12 @@ struct LongStager {
   }
 };
 
-template <int V, bool SPLIT, bool SAVE>
+template <int V, bool SPLIT, bool SAVE, bool F16>
 __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs a) {
   constexpr bool GRID = !SAVE;
+  // the state operand's type: bf16, or fp16 (F16: one operand, no saved data)
+  static_assert(!F16 || (!SPLIT && !SAVE), "the fp16 operand is a single-operand forward");
+  using Op = std::conditional_t<F16, f16x8, bf16x8>;
   using L = LongLayout<V, GRID>;
   static_assert(L::THREADS == 64 * (V / 32), "launch bounds");
   constexpr int KB = V / 32, HROW = L::HROW, NHS = L::NHS;
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   const unsigned int* zero_lds = reinterpret_cast<const unsigned int*>(lds + L::Z_OFF);
 
   // ---- prologue: chunk 0/1 inputs, W, H0 requested before the first wait
-  LongStager<V, GRID> st, st1;
+  LongStager<V, GRID, F16> st, st1;
   st.load(a, unit, row0, 0, Tb, LD);
   if (nchunks > 1) st1.load(a, unit, row0, 1, Tb, LD);
   constexpr int WLOADS = V * V / 8 / L::THREADS;
@@ -306,12 +315,20 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       G[j] = H0 ? *reinterpret_cast<const f4*>(H0 + 16 * (2 * w + j) + 4 * g) * kC : f4{0, 0, 0, 0};
+    if constexpr (F16) {
+      // an initial state beyond the fp16 operand's range is NaN from the start;
+      // with gates in [0, 1] the state never grows past max(1, max |H0|) after it
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) G[j][i] = f16_range_or_nan(G[j][i]);
+    }
   }
   // W^T fragments of this wave's two output tiles, every contraction block, via
   // LDS. Register arrays over the blocks are indexed o = 0 .. KB - 1 for block
   // (w + o) mod KB (o = 0: the wave's own block), so that every register index
   // is a compile-time constant; only LDS addresses depend on the wave.
-  bf16x8 Wf[2][KB];
+  Op Wf[2][KB];
   {
     unsigned short* wst = reinterpret_cast<unsigned short*>(lds + L::VX_OFF);
 #pragma unroll
@@ -331,8 +348,9 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
         const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)src);
         const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * HROW));
         s8 wa = s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (F16) wa = __builtin_bit_cast(s8, bf16x8_to_f16(wa));
         asm volatile("" : "=a"(wa) : "0"(wa));
-        Wf[j][o] = __builtin_bit_cast(bf16x8, wa);
+        Wf[j][o] = __builtin_bit_cast(Op, wa);
       }
     lds_barrier();  // the regions are the rank-1 stage buffers and state tiles from here on
   }
@@ -351,12 +369,12 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
 
   // operand blocks: Bf[o] lane (g, n) = bf16 G[n][32 b + 16 (j / 4) + 4 g + j % 4],
   // b = (w + o) mod KB
-  bf16x8 Bf[KB], Bl[KB];
+  Op Bf[KB], Bl[KB];
   auto make_own = [&]() {
     f8 x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) { x[i] = G[0][i]; x[4 + i] = G[1][i]; }
-    Bf[0] = __builtin_convertvector(x, bf16x8);
+    Bf[0] = __builtin_convertvector(x, Op);
     if constexpr (SPLIT) {
       const u4 hb = __builtin_bit_cast(u4, Bf[0]);
       f8 r;
@@ -370,15 +388,15 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   };
   // the shared state tile slot of step s: row n, block b at columns 32 b + 8 g
   auto publish_own = [&](int slot) {
-    *reinterpret_cast<bf16x8*>(xb + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bf[0];
-    if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(xl + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bl[0];
+    *reinterpret_cast<Op*>(xb + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bf[0];
+    if constexpr (SPLIT) *reinterpret_cast<Op*>(xl + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bl[0];
   };
   auto fetch_others = [&](int slot) {
 #pragma unroll
     for (int o = 1; o < KB; ++o) {
       const int b = (w + o) % KB;
-      Bf[o] = *reinterpret_cast<const bf16x8*>(xb + slot * 16 * HROW + n * HROW + 32 * b + 8 * g);
-      if constexpr (SPLIT) Bl[o] = *reinterpret_cast<const bf16x8*>(xl + slot * 16 * HROW + n * HROW + 32 * b + 8 * g);
+      Bf[o] = *reinterpret_cast<const Op*>(xb + slot * 16 * HROW + n * HROW + 32 * b + 8 * g);
+      if constexpr (SPLIT) Bl[o] = *reinterpret_cast<const Op*>(xl + slot * 16 * HROW + n * HROW + 32 * b + 8 * g);
     }
   };
   // rank-1 term of step s of the chunk in stage buffer sb: acc[j] = (v, tile 2w + j) x (hi, lo of c k)
@@ -413,14 +431,14 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   // with SPLIT the low halves of the state are read out too (their tiles are
   // exchanged anyway), so y carries the split operand's precision
   struct ReadoutOps {
-    bf16x8 q, s[2], sl[SPLIT ? 2 : 1];
+    Op q, s[2], sl[SPLIT ? 2 : 1];
   };
   auto readout_load = [&](int sb, int s0, int nvalid) {
     ReadoutOps r;
     const int p = g / 2, rr = 8 * (g % 2), s = s0 + p;
     s8 qv = *reinterpret_cast<const s8*>(qs_all + sb * kChunk * 16 + s * 16 + rr);
     if (n != s || p >= nvalid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
-    r.q = __builtin_bit_cast(bf16x8, qv);
+    r.q = __builtin_bit_cast(Op, qv);
     const unsigned short* src = xb + (s & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -428,13 +446,13 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
       const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * P));
       const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s4*)(src + 16 * P + 4 * HROW));
-      r.s[j] = __builtin_bit_cast(bf16x8, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      r.s[j] = __builtin_bit_cast(Op, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       if constexpr (SPLIT) {
         const unsigned short* srl = xl + (s & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
         const s4 llo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(srl + 16 * P));
         const s4 lhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s4*)(srl + 16 * P + 4 * HROW));
-        r.sl[j] = __builtin_bit_cast(bf16x8, s8{llo[0], llo[1], llo[2], llo[3], lhi[0], lhi[1], lhi[2], lhi[3]});
+        r.sl[j] = __builtin_bit_cast(Op, s8{llo[0], llo[1], llo[2], llo[3], lhi[0], lhi[1], lhi[2], lhi[3]});
       }
     }
     return r;
@@ -611,8 +629,8 @@ Plan plan_long(int B, int H, int K, int V) {
               V == 128 ? LongLayout<128, true>::TOTAL : LongLayout<64, true>::TOTAL};
 }
 
-hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream) {
-  if (!long_supports(a)) return hipErrorInvalidValue;
+hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream, bool f16) {
+  if (!long_supports(a) || (f16 && (split || a.saved))) return hipErrorInvalidValue;
   const long long grid = (long long)a.B * a.H * (a.K / 16);
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (!a.accumulate && a.y) {  // y is a sum over the row tiles
@@ -622,8 +640,13 @@ hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream) {
   }
   const dim3 block(64 * (a.V / 32)), gr((unsigned)grid);
   const bool save = a.saved != nullptr;
-#define M2RNN_LONG_LAUNCH(V_, S_, SV_) hipLaunchKernelGGL((mfma_fwd_long_kernel<V_, S_, SV_>), gr, block, 0, stream, a)
-  if (a.V == 128) {
+#define M2RNN_LONG_LAUNCH(V_, S_, SV_) hipLaunchKernelGGL((mfma_fwd_long_kernel<V_, S_, SV_, false>), gr, block, 0, stream, a)
+  if (f16) {
+    if (a.V == 128)
+      hipLaunchKernelGGL((mfma_fwd_long_kernel<128, false, false, true>), gr, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((mfma_fwd_long_kernel<64, false, false, true>), gr, block, 0, stream, a);
+  } else if (a.V == 128) {
     if (split) {
       if (save) M2RNN_LONG_LAUNCH(128, true, true); else M2RNN_LONG_LAUNCH(128, true, false);
     } else {

@@ -123,7 +123,8 @@ struct Layout {
 };
 
 // Chunk staging: each thread owns up to SLOTS_PER_THREAD 16-byte global slots.
-template <int V, int NW, bool SPLIT>
+// F16: q is staged as fp16 (the readout's operand type).
+template <int V, int NW, bool SPLIT, bool F16 = false>
 struct Stager {
   using L = Layout<V, NW, SPLIT>;
   u4 reg[L::SLOTS_PER_THREAD];
@@ -162,7 +163,7 @@ struct Stager {
   }
 
   // Publish into stage buffer `buf`: c k as a bf16 (hi, lo) pair per row, v as
-  // (v, v) pairs in [m][c] order, q raw, and the gate scalars.
+  // (v, v) pairs in [m][c] order, q (raw, or fp16 with F16), and the gate scalars.
   __device__ __forceinline__ void store(char* lds, int buf) const {
     const int tid = threadIdx.x;
     unsigned int* kx = reinterpret_cast<unsigned int*>(lds + L::KX_OFF) + buf * kChunk * L::R;
@@ -192,7 +193,10 @@ struct Stager {
       } else if (slot < L::SLOT_K + L::SLOT_Q) {
         const int s2 = slot - L::SLOT_K;
         const int s = s2 / (L::R / 8), part = s2 % (L::R / 8);
-        *reinterpret_cast<u4*>(qs + s * L::R + 8 * part) = r;
+        if constexpr (F16)
+          *reinterpret_cast<f16x8*>(qs + s * L::R + 8 * part) = bf16x8_to_f16(__builtin_bit_cast(s8, r));
+        else
+          *reinterpret_cast<u4*>(qs + s * L::R + 8 * part) = r;
       } else if (slot < L::SLOTS) {
         const int s2 = slot - L::SLOT_K - L::SLOT_Q;
         const int s = s2 / (V / 8), part = s2 % (V / 8);
@@ -217,12 +221,12 @@ struct Stager {
 };
 
 // State operand(s) for the next product from the fp32 state tiles 2b, 2b+1.
-template <bool SPLIT>
-__device__ __forceinline__ void make_operand(const f4& g0, const f4& g1, bf16x8& hi, bf16x8& lo) {
+template <bool SPLIT, typename Op>
+__device__ __forceinline__ void make_operand(const f4& g0, const f4& g1, Op& hi, Op& lo) {
   f8 x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) { x[i] = g0[i]; x[4 + i] = g1[i]; }
-  hi = __builtin_convertvector(x, bf16x8);
+  hi = __builtin_convertvector(x, Op);
   if constexpr (SPLIT) {
     // exact residual x - hi: hi widened back to fp32 from its bit pattern
     const u4 hb = __builtin_bit_cast(u4, hi);
@@ -236,9 +240,12 @@ __device__ __forceinline__ void make_operand(const f4& g0, const f4& g1, bf16x8&
   }
 }
 
-template <int V, int NW, bool SPLIT, bool SAVE>
+template <int V, int NW, bool SPLIT, bool SAVE, bool F16>
 __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   using L = Layout<V, NW, SPLIT>;
+  // the state operand's type: bf16, or fp16 (F16: one operand, no saved data)
+  static_assert(!F16 || (!SPLIT && !SAVE), "the fp16 operand is a single-operand forward");
+  using Op = std::conditional_t<F16, f16x8, bf16x8>;
   constexpr int R = L::R, CT = L::CT, KB = L::KB, HROW = L::HROW, NVX = L::NVX, NSB = L::NSB, NHS = L::NHS;
   constexpr int NPL = L::NPL;
   static_assert(KB >= 2 && CT == 2 * KB, "V must be a multiple of 32, at least 64");
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
 
   // ---- prologue. Every global read of the prologue (W, H0, chunks 0 and 1) is
   // issued before the first wait, so their latencies overlap.
-  Stager<V, NW, SPLIT> st, st1;
+  Stager<V, NW, SPLIT, F16> st, st1;
   const int nchunks = (Tb + kChunk - 1) / kChunk;
   st.load(a, unit, row0, 0, Tb);
   if (nchunks > 1) st1.load(a, unit, row0, 1, Tb);
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   // ---- W as permuted A fragments: Wf[c][b] lane (g,n) = W[32b + 16(j/4) + 4g + j%4][16c + n].
   // The head's W goes through LDS (the state-tile region, not yet in use), and
   // each fragment comes back as two transposing reads.
-  bf16x8 Wf[CT][KB];
+  Op Wf[CT][KB];
   {
     constexpr int WROW = HROW;  // padded row, as the state tiles
     static_assert(L::HB_OFF + V * WROW * 2 <= L::TOTAL, "W fits in the staging region");
@@ -309,10 +316,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
         const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)src);
         const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * WROW));
         s8 wa = s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (F16) wa = __builtin_bit_cast(s8, bf16x8_to_f16(wa));
         // pin the fragment to the accumulation registers: it is only ever a
         // matrix operand, and this leaves the arch VGPRs to the epilogue
         asm volatile("" : "=a"(wa) : "0"(wa));
-        Wf[c][b] = __builtin_bit_cast(bf16x8, wa);
+        Wf[c][b] = __builtin_bit_cast(Op, wa);
       }
     lds_barrier();  // every wave has its fragments before the region is cleared
   }
@@ -330,7 +338,15 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   f4 G[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) G[c] = h0v[c] * kC;
-  bf16x8 Bf[KB], Bl[KB];
+  if constexpr (F16) {
+    // an initial state beyond the fp16 operand's range is NaN from the start;
+    // with gates in [0, 1] the state never grows past max(1, max |H0|) after it
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) G[c][i] = f16_range_or_nan(G[c][i]);
+  }
+  Op Bf[KB], Bl[KB];
 #pragma unroll
   for (int b = 0; b < KB; ++b) make_operand<SPLIT>(G[2 * b], G[2 * b + 1], Bf[b], Bl[b]);
   // training forward: this row tile's 16-byte piece of a saved slot, per block b
@@ -382,7 +398,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
   // The step writes its own state tiles at its end, after these reads.
   constexpr int HT = CT / 2;  // tiles per readout half
   struct RO {
-    bf16x8 a[NPL][HT];  // A operand per plane (hi, lo) and 16-column tile of the half
+    Op a[NPL][HT];  // A operand per plane (hi, lo) and 16-column tile of the half
   };
   auto readout_q = [&](const Buf& B, int s0, int nvalid) {
     const int p = g / 2;                 // which step of the pair this lane group carries
@@ -390,7 +406,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     const int s = s0 + p;
     s8 qv = *reinterpret_cast<const s8*>(B.qs + s * R + 16 * w + rr);
     if (n != s || p >= nvalid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
-    return __builtin_bit_cast(bf16x8, qv);  // q_{s0 + p} in column s0 + p (p < nvalid), zero elsewhere
+    return __builtin_bit_cast(Op, qv);  // q_{s0 + p} in column s0 + p (p < nvalid), zero elsewhere
   };
   auto readout_load = [&](int s0, int half) {
     RO ro;
@@ -406,13 +422,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
         const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * P));
         const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s4*)(src + 16 * P + 4 * HROW));
-        ro.a[pl][i] = __builtin_bit_cast(bf16x8, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        ro.a[pl][i] = __builtin_bit_cast(Op, s8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
     }
     return ro;
   };
   // readout MFMA j (< NPL HT) of a half
-  auto readout_mma = [&](const RO& ro, const bf16x8& bq, int half, int j) {
+  auto readout_mma = [&](const RO& ro, const Op& bq, int half, int j) {
     const int pl = j / HT, i = j % HT;
     Dr[half * HT + i] = mfma(ro.a[pl][i], bq, Dr[half * HT + i]);
   };
@@ -529,8 +545,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
       if (t < T) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, t + 1, T, a.K, V) + rt_off + b * 1024) = Bf[b];
     }
     unsigned short* hdst = hb_w + (s & (NHS - 1)) * NPL * 16 * HROW + n * HROW + 8 * g;
-    *reinterpret_cast<bf16x8*>(hdst + 32 * b) = Bf[b];
-    if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(hdst + 16 * HROW + 32 * b) = Bl[b];
+    *reinterpret_cast<Op*>(hdst + 32 * b) = Bf[b];
+    if constexpr (SPLIT) *reinterpret_cast<Op*>(hdst + 16 * HROW + 32 * b) = Bl[b];
   };
   // training forward: the pre-activation c A_t of tiles 2b, 2b+1, as bf16
   auto save_pre = [&](int b, const f4 (&cur)[CT], int t) {
@@ -598,7 +614,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     return n_last(p) * NPU + (p == 0 ? CT : CT * NPU) + (even ? ro_halves(p) * NRH : 0);
   };
   auto mfma_unit = [&](int p, int j, f4 (&cur)[CT], f4 (&nxt)[CT], const R1& r1, const RO& roA, const RO& roB,
-                       const bf16x8& bq) {
+                       const Op& bq) {
     if (j < n_last(p) * NPU) {
       const int c = 2 * p + 2 + j / NPU;
       if (j % NPU == 0) cur[c] = mfma(Wf[c][KB - 1], Bf[KB - 1], cur[c]);
@@ -645,7 +661,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     // the previous pair's readout operands (even steps): q and the first half
     const Buf& RB = s >= 2 ? C : Cp;
     const int rs0 = s >= 2 ? s - 2 : kChunk - 2, rnv = (s >= 2 || c > 0) ? 2 : 0;
-    bf16x8 bq{};
+    Op bq{};
     RO roA{}, roB{};
     if (even) {
       bq = readout_q(RB, rs0, rnv);
@@ -725,7 +741,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
       lds_barrier();
     }
     const int te = ran - 2;  // the last pair: steps te, te + 1
-    const bf16x8 bq = readout_q(buf(c % NSB), te, min(ns - te, 2));
+    const Op bq = readout_q(buf(c % NSB), te, min(ns - te, 2));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const RO rl = readout_load(te, half);
@@ -756,8 +772,9 @@ __global__ void zero_fill_kernel(float* p, long long n) {
   for (; i < n; i += stride) p[i] = 0.0f;
 }
 
-template <int V, int NW, bool SPLIT>
+template <int V, int NW, bool SPLIT, bool F16 = false>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
+  if (F16 && a.saved) return hipErrorInvalidValue;  // the training forward saves bf16 operands
   constexpr int R = 16 * NW;
   const int splits = a.K / R;
   const long long grid = (long long)a.B * a.H * splits;
@@ -769,10 +786,14 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     hipError_t e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream);
     if (e != hipSuccess) return e;
   }
-  if (a.saved)
-    hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, SPLIT, true>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
+  if constexpr (F16)
+    hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, false, false, true>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
+  else if (a.saved)
+    hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, SPLIT, true, false>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+                       a);
   else
-    hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, SPLIT, false>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((mfma_fwd_kernel<V, NW, SPLIT, false, false>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+                       a);
   return hipGetLastError();
 }
 
@@ -820,10 +841,14 @@ Plan plan_mfma(int B, int H, int K, int V, bool split) {
   return Plan{grid > 0x7fffffffLL ? -1 : (int)grid, 64 * nw, R, splits, splits > 1 ? 1 : 0, lds};
 }
 
-hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream) {
-  if (!mfma_supports(a.K, a.V, a.bf16)) return hipErrorInvalidValue;
+hipError_t launch_mfma(const FwdArgs& a, bool split, hipStream_t stream, bool f16) {
+  if (!mfma_supports(a.K, a.V, a.bf16) || (split && f16)) return hipErrorInvalidValue;
   if (decode_supports(a)) return launch_decode(a, stream);  // one step: the decoding kernel
   const int nw = pick_nw(a.K);
+  if (f16) {
+    if (a.V == 128) return nw == 4 ? launch_t<128, 4, false, true>(a, stream) : launch_t<128, 2, false, true>(a, stream);
+    return nw == 4 ? launch_t<64, 4, false, true>(a, stream) : launch_t<64, 2, false, true>(a, stream);
+  }
   if (split) {
     if (a.V == 128) return nw == 4 ? launch_t<128, 4, true>(a, stream) : launch_t<128, 2, true>(a, stream);
     return nw == 4 ? launch_t<64, 4, true>(a, stream) : launch_t<64, 2, true>(a, stream);

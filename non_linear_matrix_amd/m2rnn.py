@@ -23,7 +23,7 @@ HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__fil
 STATUS = {0: "M2RNN_SUCCESS", 1: "M2RNN_ERROR_INVALID_VALUE", 2: "M2RNN_ERROR_NOT_SUPPORTED", 3: "M2RNN_ERROR_LAUNCH",
           4: "M2RNN_ERROR_SCRATCH_TOO_SMALL"}
 ALGOS = {"auto": 0, "simple": 1, "mfma": 2, "mfma_split": 3, "mfma_long": 4, "mfma_long_split": 5,
-         "mfma_f32": 6}
+         "mfma_f32": 6, "mfma_f16": 7, "mfma_long_f16": 8}
 DTYPES = {"f32": 0, "bf16": 1}
 FLAG_ACCUMULATE_Y = 1
 FLAG_DETERMINISTIC = 2

@@ -32,7 +32,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-__all__ = ["widen", "m2rnn_fwd_ref", "round_to_bf16"]
+__all__ = ["widen", "m2rnn_fwd_ref", "round_to_bf16", "round_to_f16"]
 
 
 def widen(x: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
@@ -54,6 +54,13 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
     u = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) & np.uint64(0xFFFF0000)
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def round_to_f16(x: np.ndarray) -> np.ndarray:
+    """Diagnostic only: value of x (fp64) rounded to fp32, then to IEEE binary16
+    (RNE, subnormals kept, overflow to infinity)."""
+    with np.errstate(over="ignore"):
+        return x.astype(np.float32).astype(np.float16).astype(np.float64)
 
 
 def m2rnn_fwd_ref(
@@ -78,9 +85,10 @@ def m2rnn_fwd_ref(
     Returns (y [B,H,T,V], H_T [B,H,K,V]) in fp64, plus all states
     [B,H,T,K,V] when ``return_states``.
 
-    ``state_rounding="bf16"`` is a diagnostic variant (not the definition): the
-    state is rounded to bfloat16 before each product with W, to estimate how
-    much a bf16-operand matrix product perturbs the trajectory.
+    ``state_rounding="bf16"`` (or ``"f16"``) is a diagnostic variant (not the
+    definition): the state is rounded to bfloat16 (IEEE binary16) before each
+    product with W, to estimate how much a matrix product on such an operand
+    perturbs the trajectory.
     """
     kk, vv, qq, ff, WW = (widen(a, dtype) for a in (k, v, q, f, W))
     B, H, T, K = kk.shape
@@ -103,7 +111,7 @@ def m2rnn_fwd_ref(
     states = np.empty((B, H, T, K, V), dtype=np.float64) if return_states else None
     Wb = WW[None, :, :, :]  # the per-head matrix, shared by every batch row
     for t in range(T):
-        S_in = round_to_bf16(S) if state_rounding == "bf16" else S
+        S_in = round_to_bf16(S) if state_rounding == "bf16" else round_to_f16(S) if state_rounding == "f16" else S
         A = np.matmul(S_in, Wb)                                       # H_{t-1} W
         outer = kk[:, :, t, :, None] * vv[:, :, t, None, :]           # k_t v_t^T
         Z = np.tanh(A + outer)

@@ -7,11 +7,11 @@ the full sequence length, it reports:
   (i)  how a 1e-9 perturbation of the initial state grows along the sequence:
        growth = max|H_T(H0 + d) - H_T(H0)| / 1e-9 per unit (a chaotic trajectory
        would make any rounding difference explode; a contracting one forgets it);
-  (ii) the normwise error of the diagnostic run that rounds the state to
-       bfloat16 before every product with W (the oracle's `state_rounding`
-       mode), against the exact run: an estimate of the error a single
-       bf16-operand matrix product adds on its own, per output tensor and for
-       the worst unit.
+  (ii) the normwise error of the diagnostic runs that round the state to
+       bfloat16, and to fp16, before every product with W (the oracle's
+       `state_rounding` modes), against the exact run: an estimate of the error
+       a single bf16- or fp16-operand matrix product adds on its own, per output
+       tensor and for the worst unit.
 Usage: python -m oracle.preflight [--units N] [C1 C2 ...]
 """
 from __future__ import annotations
@@ -59,12 +59,13 @@ def run(name, max_units=None, seed=0):
     line = (f"{name}: T={cfg.T} units={len(units)} | perturbation growth of H_T: max {growth.max():.3g} "
             f"median {np.median(growth):.3g}")
     if cfg.dtype == "bf16":
-        yr, HTr = m2rnn_fwd_ref(x["k"], x["v"], x["q"], x["f"], x["W"], x["H0"], dtype=cfg.dtype,
-                                state_rounding="bf16")
-        uy, uh = _unit_err(yr, y)[0], _unit_err(HTr, HT)[0]
-        wy, wh = int(np.argmax(uy)), int(np.argmax(uh))
-        line += (f" | bf16-state diagnostic: y {_err(yr, y):.3e} H_T {_err(HTr, HT):.3e}; worst unit y "
-                 f"{units[wy]} {uy[wy]:.3e}, H_T {units[wh]} {uh[wh]:.3e}")
+        for mode in ("bf16", "f16"):
+            yr, HTr = m2rnn_fwd_ref(x["k"], x["v"], x["q"], x["f"], x["W"], x["H0"], dtype=cfg.dtype,
+                                    state_rounding=mode)
+            uy, uh = _unit_err(yr, y)[0], _unit_err(HTr, HT)[0]
+            wy, wh = int(np.argmax(uy)), int(np.argmax(uh))
+            line += (f" | {mode}-state diagnostic: y {_err(yr, y):.3e} H_T {_err(HTr, HT):.3e}; worst unit y "
+                     f"{units[wy]} {uy[wy]:.3e}, H_T {units[wh]} {uh[wh]:.3e}")
     line += f" | max|y| {np.max(np.abs(y)):.3g} max|H_T| {np.max(np.abs(HT)):.3g} | {time.time() - t0:.1f}s"
     print(line, flush=True)
 

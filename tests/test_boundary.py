@@ -28,7 +28,7 @@ def _check(**over):
 def test_library_exists_and_loads():
     assert os.path.exists(m2rnn.LIB_PATH), "build the library first (python -m non_linear_matrix_amd.build)"
     lib = m2rnn.load()
-    assert m2rnn.version() == 900
+    assert m2rnn.version() == 1000
 
 
 def test_every_declared_symbol_is_exported():
@@ -118,7 +118,7 @@ def test_mfma_f32_coverage():
 
 def test_launch_plans():
     p = m2rnn.get_plan(8, 16, 2048, 128, 128, "bf16", "auto")
-    assert p["algo"] == "mfma_split" and p["grid"] == 256 and p["block"] == 256
+    assert p["algo"] == "mfma_f16" and p["grid"] == 256 and p["block"] == 256
     assert p["rows_per_group"] == 64 and p["groups_per_unit"] == 2 and p["clears_y"] == 1
     assert p["lds_bytes"] <= 160 * 1024
     p = m2rnn.get_plan(2, 16, 32768, 64, 128, "bf16", "mfma")
@@ -150,21 +150,21 @@ def test_unknown_flag_bits_are_rejected():
 
 
 def test_auto_picks_a_kernel_that_covers_the_shape():
-    assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "bf16") == "mfma_split"     # 1024 row tiles
+    assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "bf16") == "mfma_f16"     # 1024 row tiles
     assert m2rnn.pick_algo(1, 1, 64, 16, 16, "f32") == "mfma_f32"
     assert m2rnn.pick_algo(1, 1, 64, 16, 96, "bf16") == "simple"
     # up to 768 16-row tiles: the latency-oriented kernel
-    assert m2rnn.pick_algo(1, 1, 64, 16, 128, "bf16") == "mfma_long_split"
-    assert m2rnn.pick_algo(1, 32, 8192, 128, 128, "bf16") == "mfma_long_split"
-    assert m2rnn.pick_algo(2, 16, 32768, 64, 128, "bf16") == "mfma_long_split"
-    assert m2rnn.pick_algo(4, 8, 512, 64, 64, "bf16") == "mfma_long_split"
-    assert m2rnn.pick_algo(6, 16, 100, 128, 128, "bf16") == "mfma_long_split"  # 768 tiles
-    assert m2rnn.pick_algo(7, 16, 100, 128, 128, "bf16") == "mfma_split"       # 896 tiles
-    assert m2rnn.pick_algo(1, 32, 1, 128, 128, "bf16") == "mfma_split"         # one step: decoding kernel
+    assert m2rnn.pick_algo(1, 1, 64, 16, 128, "bf16") == "mfma_long_f16"
+    assert m2rnn.pick_algo(1, 32, 8192, 128, 128, "bf16") == "mfma_long_f16"
+    assert m2rnn.pick_algo(2, 16, 32768, 64, 128, "bf16") == "mfma_long_f16"
+    assert m2rnn.pick_algo(4, 8, 512, 64, 64, "bf16") == "mfma_long_f16"
+    assert m2rnn.pick_algo(6, 16, 100, 128, 128, "bf16") == "mfma_long_f16"  # 768 tiles
+    assert m2rnn.pick_algo(7, 16, 100, 128, 128, "bf16") == "mfma_f16"       # 896 tiles
+    assert m2rnn.pick_algo(1, 32, 1, 128, 128, "bf16") == "mfma_f16"         # one step: decoding kernel
     assert m2rnn.pick_algo(1, 4, 64, 32, 64, "f32") == "mfma_f32"
     assert m2rnn.pick_algo(8, 16, 2048, 128, 128, "f32") == "mfma_f32"
     p = m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "auto")
-    assert p["algo"] == "mfma_long_split" and p["grid"] == 256 and p["block"] == 256 and p["clears_y"] == 1
+    assert p["algo"] == "mfma_long_f16" and p["grid"] == 256 and p["block"] == 256 and p["clears_y"] == 1
 
 
 def test_decoding_plan():
@@ -202,27 +202,28 @@ def test_deterministic_flag_and_the_long_kernels():
 def test_deterministic_auto_resolves_to_a_covering_repeatable_kernel():
     """AUTO under M2RNN_FLAG_DETERMINISTIC keeps its choice unless the call also
     accumulates into y from two or more workgroups: then it takes the multi-step
-    split kernel where that has one workgroup per unit, else the simple kernel.
+    kernel with the same operand where that has one workgroup per unit, else the
+    simple kernel.
     Host only: the plan query launches nothing."""
     det, acc = m2rnn.FLAG_DETERMINISTIC, m2rnn.FLAG_ACCUMULATE_Y
     # the long kernel stays under the flag alone, for every K
     for K in (16, 32, 48, 64, 80, 96, 112, 128):
-        assert m2rnn.get_plan(2, 3, 37, K, 128, "bf16", "auto", det)["algo"] == "mfma_long_split", K
-    assert m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "auto", det)["algo"] == "mfma_long_split"
+        assert m2rnn.get_plan(2, 3, 37, K, 128, "bf16", "auto", det)["algo"] == "mfma_long_f16", K
+    assert m2rnn.get_plan(1, 32, 8192, 128, 128, "bf16", "auto", det)["algo"] == "mfma_long_f16"
     # accumulating: the multi-step kernel where it runs one workgroup per unit
-    assert m2rnn.get_plan(2, 3, 37, 32, 128, "bf16", "auto", det | acc)["algo"] == "mfma_split"
-    assert m2rnn.get_plan(2, 3, 37, 64, 128, "bf16", "auto", det | acc)["algo"] == "mfma_split"
+    assert m2rnn.get_plan(2, 3, 37, 32, 128, "bf16", "auto", det | acc)["algo"] == "mfma_f16"
+    assert m2rnn.get_plan(2, 3, 37, 64, 128, "bf16", "auto", det | acc)["algo"] == "mfma_f16"
     # ... and the simple kernel where it does not cover the shape (K = 48, ...) or
     # runs two workgroups (K = 128); one row tile stays on the long kernel
     for K in (48, 80, 96, 112, 128):
         assert m2rnn.get_plan(2, 3, 37, K, 128, "bf16", "auto", det | acc)["algo"] == "simple", K
-    assert m2rnn.get_plan(2, 3, 37, 16, 128, "bf16", "auto", det | acc)["algo"] == "mfma_long_split"
+    assert m2rnn.get_plan(2, 3, 37, 16, 128, "bf16", "auto", det | acc)["algo"] == "mfma_long_f16"
     # K = 128 on the multi-step kernel: two workgroups add into a cleared y
-    assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", det)["algo"] == "mfma_split"
+    assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", det)["algo"] == "mfma_f16"
     assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", det | acc)["algo"] == "simple"
     # without the flag nothing changes
-    assert m2rnn.get_plan(2, 3, 37, 48, 128, "bf16", "auto")["algo"] == "mfma_long_split"
-    assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", acc)["algo"] == "mfma_split"
+    assert m2rnn.get_plan(2, 3, 37, 48, 128, "bf16", "auto")["algo"] == "mfma_long_f16"
+    assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", "auto", acc)["algo"] == "mfma_f16"
 
 
 def test_deterministic_accumulate_refuses_two_atomic_groups():
@@ -373,3 +374,47 @@ def test_frontend_validates_before_launching():
     assert call(D=60) == UNSUPPORTED         # rows of x must be whole 16-byte pieces
     assert call(K=40) == UNSUPPORTED
     assert call(dt=m2rnn.DTYPES["f32"]) == UNSUPPORTED
+
+
+def test_f16_operand_families():
+    """MFMA_F16 covers the multi-step kernel's shapes and MFMA_LONG_F16 the long
+    kernel's (bf16 inputs only); with the deterministic flag and accumulation AUTO
+    never resolves to them, a deterministic call keeps them where their y adds are
+    order-free and refuses them where two or more row groups would add into the
+    caller's y; no training entry point takes them. All host-side, before any
+    launch."""
+    lib = m2rnn.load()
+    p = 0x10000
+    bf16, f32 = m2rnn.DTYPES["bf16"], m2rnn.DTYPES["f32"]
+    det, acc = m2rnn.FLAG_DETERMINISTIC, m2rnn.FLAG_ACCUMULATE_Y
+    for K in (32, 64, 128):
+        for V in (64, 128):
+            assert _check(K=K, V=V, algo="mfma_f16") == OK
+    assert _check(K=16, V=128, algo="mfma_f16") == UNSUPPORTED
+    assert _check(dtype="f32", algo="mfma_f16") == UNSUPPORTED
+    for K in (16, 48, 128):
+        assert _check(K=K, V=128, algo="mfma_long_f16") == OK
+    assert _check(K=64, V=96, algo="mfma_long_f16") == UNSUPPORTED
+    assert _check(dtype="f32", algo="mfma_long_f16") == UNSUPPORTED
+    # plans: the kernels of the bf16 single-operand families
+    for algo, ref in (("mfma_f16", "mfma"), ("mfma_long_f16", "mfma_long")):
+        a, b = m2rnn.get_plan(8, 16, 2048, 128, 128, "bf16", algo), m2rnn.get_plan(8, 16, 2048, 128, 128, "bf16", ref)
+        assert a["algo"] == algo and {k: v for k, v in a.items() if k != "algo"} == \
+            {k: v for k, v in b.items() if k != "algo"}
+        assert m2rnn.get_plan(8, 16, 64, 128, 128, "bf16", algo, det)["algo"] == algo
+    # deterministic + accumulate: two workgroups (K = 128) or several row tiles refused
+    with pytest.raises(m2rnn.M2RNNError):
+        m2rnn.get_plan(2, 2, 40, 128, 128, "bf16", "mfma_f16", det | acc)
+    with pytest.raises(m2rnn.M2RNNError):
+        m2rnn.get_plan(2, 2, 40, 32, 128, "bf16", "mfma_long_f16", det | acc)
+    assert m2rnn.get_plan(2, 2, 40, 64, 128, "bf16", "mfma_f16", det | acc)["algo"] == "mfma_f16"
+    # the training forwards and the backward pass refuse them
+    for algo in ("mfma_f16", "mfma_long_f16"):
+        a = m2rnn.ALGOS[algo]
+        assert lib.m2rnn_fwd_save(p, p, p, p, p, None, p, None, p, 2, 2, 16, 64, 64, bf16, a, None) == UNSUPPORTED
+        assert lib.m2rnn_fwd_ckpt(p, p, p, p, p, None, p, None, p, 2, 2, 64, 64, 64, 16, bf16, a, None) == UNSUPPORTED
+        assert lib.m2rnn_bwd_recompute(p, p, p, p, p, None, p, p, None, p, p, p, p, p, None, p,
+                                       2, 2, 64, 64, 64, 16, bf16, a, None) == UNSUPPORTED
+        assert lib.m2rnn_bwd_algo(p, p, p, p, p, None, p, p, None, p, p, p, p, p, None, p, 2, 2, 16, 64, 64, bf16,
+                                  a, None) == UNSUPPORTED
+        assert lib.m2rnn_fwd_save(p, p, p, p, p, None, p, None, p, 2, 2, 16, 64, 64, f32, a, None) == UNSUPPORTED

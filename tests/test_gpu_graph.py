@@ -53,7 +53,7 @@ def _replay_check(fn, outs, eager, close=()):
                 assert torch.equal(o, e), f"replay {r}, output {i}"
 
 
-@pytest.mark.parametrize("algo", ["mfma", "mfma_split"])
+@pytest.mark.parametrize("algo", ["mfma", "mfma_split", "mfma_f16"])
 def test_forward_replays(algo):
     import torch
     from non_linear_matrix_amd import m2rnn

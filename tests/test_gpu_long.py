@@ -116,28 +116,29 @@ def test_ragged_lengths_and_accumulate():
 
 
 def test_auto_takes_the_long_kernel_and_is_repeatable():
-    """AUTO on a small-batch shape is the split long kernel, with or without the
-    deterministic flag: its row tiles' readouts go onto a common grid, so y is
-    bit for bit the same from run to run. With the flag and accumulation the
-    call leaves the long kernel (several row tiles would add into the caller's y)."""
+    """AUTO on a small-batch shape is the long kernel with the fp16 operand, with
+    or without the deterministic flag: its row tiles' readouts go onto a common
+    grid, so y is bit for bit the same from run to run. With the flag and
+    accumulation the call leaves the long kernel (several row tiles would add
+    into the caller's y)."""
     import torch
     from non_linear_matrix_amd import m2rnn
     cfg = scaled(CONFIGS["C5"], B=1, H=2, T=100)
     announce("AUTO / deterministic flag")
     x = generate(cfg, 65)
     yA, HA = gpu_run(x, algo="auto")
-    yL, HL = gpu_run(x, algo="mfma_long_split")
+    yL, HL = gpu_run(x, algo="mfma_long_f16")
     assert np.array_equal(HA, HL) and np.array_equal(yA, yL)
     yD1, HD1 = gpu_run(x, algo="auto", deterministic=True)
     yD2, HD2 = gpu_run(x, algo="auto", deterministic=True)
     assert np.array_equal(yD1, yA) and np.array_equal(HD1, HA)
     assert np.array_equal(yD1, yD2) and np.array_equal(HD1, HD2)
-    # accumulating under the flag: the multi-step split kernel (one workgroup at K = 64)
+    # accumulating under the flag: the multi-step kernel (one workgroup at K = 64)
     d = to_device(x)
     y0 = torch.zeros((1, 2, cfg.T, cfg.V), dtype=torch.float32, device="cuda")
     m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], y=y0, accumulate_y=True, deterministic=True)
     torch.cuda.synchronize()
-    yS, HS = gpu_run(x, algo="mfma_split")
+    yS, HS = gpu_run(x, algo="mfma_f16")
     assert np.array_equal(y0.cpu().numpy(), yS)
     # a single step under the flag: the decoding kernel, which has no atomics
     one = scaled(cfg, T=1)
@@ -165,12 +166,13 @@ def test_repeatable_with_a_large_initial_state(K):
 
 @pytest.mark.parametrize("name", ["C2", "C4", "C5"])
 def test_default_forward_is_bitwise_repeatable(name):
-    """The library's default forward (AUTO: the split long kernel on these
-    workloads) at full size gives the same y and H_T bit for bit on every run,
-    although a unit's K/16 row tiles add into y in whatever order they finish."""
+    """The library's default forward (AUTO: the long kernel with the fp16 operand
+    on these workloads) at full size gives the same y and H_T bit for bit on
+    every run, although a unit's K/16 row tiles add into y in whatever order they
+    finish."""
     from non_linear_matrix_amd import m2rnn
     cfg = CONFIGS[name]
-    assert m2rnn.pick_algo(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V, cfg.dtype) == "mfma_long_split"
+    assert m2rnn.pick_algo(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V, cfg.dtype) == "mfma_long_f16"
     announce(f"{name} full size, default forward, repeatability")
     x = generate(cfg, 0)
     y1, H1 = gpu_run(x)

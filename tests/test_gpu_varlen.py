@@ -11,8 +11,8 @@ from oracle import m2rnn_fwd_ref
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"mfma": 2e-2, "mfma_split": 2e-2, "simple": 1e-4}
-ALGOS = ("mfma", "mfma_split", "simple")
+TOL = {"mfma": 2e-2, "mfma_split": 2e-2, "mfma_f16": 2e-2, "simple": 1e-4}
+ALGOS = ("mfma", "mfma_split", "mfma_f16", "simple")
 
 
 @pytest.fixture(scope="module", autouse=True)

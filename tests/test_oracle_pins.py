@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 from decimal_ref import fwd_decimal
-from oracle import m2rnn_fwd_ref, round_to_bf16
+from oracle import m2rnn_fwd_ref, round_to_bf16, round_to_f16
 from non_linear_matrix_amd.inputs import CONFIGS, generate, scaled
 
 
@@ -287,3 +287,20 @@ def test_bf16_state_rounding_diagnostic_stays_close(fwd=FWD):
     assert 0 < _nrm(yr, y) < 2e-2 and 0 < _nrm(HTr, HT) < 2e-2
     r = round_to_bf16(np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5]))
     assert list(r) == [1.0, 1.0 + 2.0 ** -6, -2.5]
+
+
+def test_f16_state_rounding_diagnostic(fwd=FWD):
+    """The fp16-state variant: closer to the definition than the bf16 one (2^-12
+    against 2^-9 relative rounding per step), and its rounding is IEEE binary16's
+    round to nearest even: ties to the even neighbour, subnormals down to 2^-24,
+    overflow past 65504 + 16 to infinity."""
+    cfg = scaled(CONFIGS["C2"], B=1, H=2, T=64)
+    x = generate(cfg, seed=0)
+    y, HT = fwd(x["k"], x["v"], x["q"], x["f"], x["W"], x["H0"], dtype="bf16")
+    yb, HTb = fwd(x["k"], x["v"], x["q"], x["f"], x["W"], x["H0"], dtype="bf16", state_rounding="bf16")
+    yh, HTh = fwd(x["k"], x["v"], x["q"], x["f"], x["W"], x["H0"], dtype="bf16", state_rounding="f16")
+    assert 0 < _nrm(yh, y) < _nrm(yb, y) and 0 < _nrm(HTh, HT) < _nrm(HTb, HT)
+    r = round_to_f16(np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, -2.5, 65519.0, 65520.0,
+                               2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14 * (1 + 2.0 ** -10)]))
+    assert list(r[:4]) == [1.0, 1.0 + 2.0 ** -9, -2.5, 65504.0]
+    assert np.isinf(r[4]) and r[5] == 0.0 and r[6] == 2.0 ** -24 and r[7] == 2.0 ** -14 * (1 + 2.0 ** -10)
