@@ -38,14 +38,14 @@ METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
     # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
-    ("C3", "mfma"): (136498.6, 270336.0, "m2rnn_mfma.hip",
-                     "61a0b38786d31a5bfc5785af7dd0ab18ba457c5234035cc16cffff1f6fc6d02b"),
+    ("C3", "mfma_f16"): (136565.0, 270336.0, "m2rnn_mfma.hip",
+                         "0436cbb1844c14948cf1a80575cee4dd920a6a24bc5cc080a2ef9585a0b554dd"),
     ("D1", "decode"): (267349.0, 528389.4, "m2rnn_decode.hip",
-                     "d6f09bfc7c21aa0dc4fc5e513ca60a152b47059c85446459709af8e502678a47"),
-    ("C4", "mfma_long_split"): (669893.3, 1050624.0, "m2rnn_long.hip",
-                                "efcf06bc279dd92f541895dcbec5a34b5a7d1b3424b485541ca93b8934495259"),
-    ("C5", "mfma_long_split"): (1053893.0, 2098176.0, "m2rnn_long.hip",
-                                "efcf06bc279dd92f541895dcbec5a34b5a7d1b3424b485541ca93b8934495259"),
+                       "d6f09bfc7c21aa0dc4fc5e513ca60a152b47059c85446459709af8e502678a47"),
+    ("C4", "mfma_long_f16"): (669879.4, 1050624.0, "m2rnn_long.hip",
+                              "0d82479c29d5ff572480cd114441b6c5a1dcd757598948d66bd6d7235887bbbc"),
+    ("C5", "mfma_long_f16"): (1053878.5, 2098176.0, "m2rnn_long.hip",
+                              "0d82479c29d5ff572480cd114441b6c5a1dcd757598948d66bd6d7235887bbbc"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the

@@ -151,3 +151,40 @@ def test_training_entry_points_refuse_the_f16_families():
         with pytest.raises(RuntimeError):
             m2rnn.fwd_save(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], algo=algo)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("algo", ["mfma_f16", "mfma_long_f16"])
+def test_values_beyond_the_fp16_range_give_nan(algo):
+    """One W, q or H0 value beyond the fp16 operand's range makes the outputs it
+    reaches NaN, never a finite wrong value; in range (65504 itself) all is finite.
+    The split operand (full bf16 range) keeps every output finite."""
+    from non_linear_matrix_amd.inputs import fp32_to_bf16_bits
+    cfg = scaled(CONFIGS["C3"], B=1, H=2, K=64, V=128, T=20)
+    base = generate(cfg, 12)
+    big = fp32_to_bf16_bits(np.array([1.0e5], np.float32))[0]
+    edge = fp32_to_bf16_bits(np.array([65280.0], np.float32))[0]   # the largest bf16 below 65504
+
+    def case(what):
+        x = {k: (None if a is None else a.copy()) for k, a in base.items()}
+        if what == "W":
+            x["W"][1, 3, 5] = big
+        elif what == "q":
+            x["q"][0, 1, 7, 2] = big
+        elif what == "H0":
+            x["H0"][0, 1, 4, 9] = 3.0e4
+        elif what == "W_edge":
+            x["W"][1, 3, 5] = edge
+        return x
+
+    announce(f"fp16 range, algo={algo}")
+    for what in ("W", "H0"):
+        y, HT = gpu_run(case(what), algo=algo)
+        assert np.all(np.isfinite(y[:, 0])) and np.all(np.isfinite(HT[:, 0])), what   # head 0 untouched
+        assert np.any(np.isnan(HT[:, 1])) and np.any(np.isnan(y[:, 1])), what
+        ys, HTs = gpu_run(case(what), algo="mfma_split")
+        assert np.all(np.isfinite(ys)) and np.all(np.isfinite(HTs)), what
+    y, HT = gpu_run(case("q"), algo=algo)
+    assert np.all(np.isnan(y[0, 1, 7])) and np.all(np.isfinite(HT)), "q"
+    assert np.all(np.isfinite(np.delete(y[0, 1], 7, axis=0)))
+    y, HT = gpu_run(case("W_edge"), algo=algo)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(HT)), "W at 65280"
