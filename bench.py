@@ -42,10 +42,10 @@ TRAFFIC_KIB = {
                          "0436cbb1844c14948cf1a80575cee4dd920a6a24bc5cc080a2ef9585a0b554dd"),
     ("D1", "decode"): (267349.0, 528389.4, "m2rnn_decode.hip",
                        "d6f09bfc7c21aa0dc4fc5e513ca60a152b47059c85446459709af8e502678a47"),
-    ("C4", "mfma_long_f16"): (669879.4, 1050624.0, "m2rnn_long.hip",
-                              "0d82479c29d5ff572480cd114441b6c5a1dcd757598948d66bd6d7235887bbbc"),
-    ("C5", "mfma_long_f16"): (1053878.5, 2098176.0, "m2rnn_long.hip",
-                              "0d82479c29d5ff572480cd114441b6c5a1dcd757598948d66bd6d7235887bbbc"),
+    ("C4", "mfma_long_f16"): (669879.6, 1050624.0, "m2rnn_long.hip",
+                              "77f5455b82cd955bb1e03536c2bd0ee2ca06053b2522b09b376819a89569f855"),
+    ("C5", "mfma_long_f16"): (1053879.0, 2098176.0, "m2rnn_long.hip",
+                              "77f5455b82cd955bb1e03536c2bd0ee2ca06053b2522b09b376819a89569f855"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the

@@ -106,8 +106,9 @@ typedef enum m2rnn_dtype {
  * MFMA_LONG, MFMA_LONG_SPLIT: the same arithmetic as MFMA / MFMA_SPLIT, for
  *             workloads with few 16-row tiles (B H K / 16 well below the GPU's
  *             1024 SIMDs: small batches, long sequences). Each tile's V columns
- *             are spread over V/32 waves that exchange the state operand through
- *             LDS every step, which cuts the per-step latency; each tile is its
+ *             are spread over V/32 waves (V/16 at V = 64, except in the training
+ *             forwards) that exchange the state operand through LDS every step,
+ *             which cuts the per-step latency; each tile is its
  *             own workgroup, so y is summed over a unit's K/16 tiles with atomic
  *             adds. Each tile's contribution to y_t is first rounded to a grid of
  *             spacing 2^(E-23), where 2^E > 1.0625 ||q_t||_1 M_t bounds |y_t|

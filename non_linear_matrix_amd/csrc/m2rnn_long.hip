@@ -9,7 +9,8 @@
 // wave's whole product and epilogue (~1900 cycles at V = 128) and a workload
 // with fewer tiles than the GPU has SIMDs leaves most of them idle. Here a tile
 // is one workgroup of V/32 waves, each owning 32 columns (two 16-column output
-// tiles, one 32-wide contraction block):
+// tiles, one 32-wide contraction block), or at V = 64 of V/16 waves, each
+// owning one 16-column output tile (half a block):
 //   * a wave's products are its two output tiles against all V/32 operand
 //     blocks (W^T fragments of its columns only, in AGPRs); the epilogue covers
 //     its 8 elements per lane;
@@ -51,9 +52,13 @@ constexpr int kChunk = 16;
 // GRID: the y grid of the plain forward (the training forward keeps its y adds
 // unrounded and stages only its own rows of q, which keeps it within the
 // registers of two workgroups per CU).
-template <int V, bool GRID>
+// TW: 16-column output tiles per wave (2: V/32 waves, each owning a 32-wide
+// contraction block; 1: V/16 waves, two per block, so a step's epilogue and
+// products are split over twice the waves).
+template <int V, bool GRID, int TW = 2>
 struct LongLayout {
-  static constexpr int S = V / 32;        // waves per workgroup = column blocks
+  static_assert(TW == 1 || TW == 2, "one or two output tiles per wave");
+  static constexpr int S = V / (16 * TW);  // waves per workgroup
   static constexpr int CT = V / 16;       // 16-column tiles
   static constexpr int THREADS = 64 * S;
   static constexpr int HROW = V + 8;      // bf16 per state-tile row (padded)
@@ -101,8 +106,10 @@ struct LongLayout {
   // GRID: q of every row (K <= 128: 16 pieces per step), its own registers. Piece
   // i = tid + j THREADS is step i / 16, part i % 16, so a step's pieces fill one
   // 16-lane DPP row.
-  static constexpr int QPT = GRID ? kChunk * 16 / THREADS : 0;
-  static_assert(!GRID || QPT * THREADS == kChunk * 16, "whole q pieces per thread");
+  // (with more than 256 threads the first 256 take one piece each)
+  static constexpr int QPT = GRID ? (kChunk * 16 + THREADS - 1) / THREADS : 0;
+  static_assert(!GRID || QPT * THREADS == kChunk * 16 || (QPT == 1 && THREADS % (kChunk * 16) == 0),
+                "whole q pieces per thread");
 };
 
 // Product over the 16 lanes of a DPP row; every lane of the row ends with it
@@ -118,9 +125,9 @@ __device__ __forceinline__ float row_prod16(float x) {
 // One chunk of per-step inputs for the tile's 16 rows: loaded to registers, then
 // stored into a stage buffer in the forms the MFMAs read.
 // F16: q is staged as fp16 (the readout's operand type)
-template <int V, bool GRID, bool F16 = false>
+template <int V, bool GRID, bool F16 = false, int TW = 2>
 struct LongStager {
-  using L = LongLayout<V, GRID>;
+  using L = LongLayout<V, GRID, TW>;
   // 8 staged q values (bf16 bit patterns) as stored in LDS
   static __device__ __forceinline__ u4 q_out(const u4& r) {
     if constexpr (F16) return __builtin_bit_cast(u4, bf16x8_to_f16(__builtin_bit_cast(s8, r)));
@@ -158,7 +165,8 @@ struct LongStager {
       for (int j = 0; j < L::QPT; ++j) {
         const int i = tid + j * L::THREADS, t = t0 + i / 16, col = 8 * (i % 16);
         qreg[j] = u4{0, 0, 0, 0};
-        if (t < Tb && col < a.K) qreg[j] = *reinterpret_cast<const u4*>(q + (unit * ld + t) * a.K + col);
+        if (i < kChunk * 16 && t < Tb && col < a.K)
+          qreg[j] = *reinterpret_cast<const u4*>(q + (unit * ld + t) * a.K + col);
       }
     }
     freg = 0x3f80u;  // gate 1 past the end: the padding steps keep the state
@@ -179,6 +187,7 @@ struct LongStager {
 #pragma unroll
     for (int j = 0; j < L::QPT; ++j) {
       const int i = tid + j * L::THREADS, st = i / 16, own = i % 16 - row0 / 8;
+      if (i >= kChunk * 16) break;  // whole waves past the chunk's pieces
       float qa = 0.0f;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -244,14 +253,15 @@ struct LongStager {
   }
 };
 
-template <int V, bool SPLIT, bool SAVE, bool F16>
-__global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs a) {
+template <int V, bool SPLIT, bool SAVE, bool F16, int TW>
+__global__ __launch_bounds__(64 * V / (16 * TW), 1) void mfma_fwd_long_kernel(FwdArgs a) {
   constexpr bool GRID = !SAVE;
+  static_assert(TW == 2 || !SAVE, "the saving forward keeps two tiles per wave (whole saved blocks)");
   // the state operand's type: bf16, or fp16 (F16: one operand, no saved data)
   static_assert(!F16 || (!SPLIT && !SAVE), "the fp16 operand is a single-operand forward");
   using Op = std::conditional_t<F16, f16x8, bf16x8>;
-  using L = LongLayout<V, GRID>;
-  static_assert(L::THREADS == 64 * (V / 32), "launch bounds");
+  using L = LongLayout<V, GRID, TW>;
+  static_assert(L::THREADS == 64 * V / (16 * TW), "launch bounds");
   constexpr int KB = V / 32, HROW = L::HROW, NHS = L::NHS;
   __shared__ __attribute__((aligned(16))) char lds[L::TOTAL];
 
@@ -266,6 +276,9 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   const int Tb = a.lens ? min(max(a.lens[unit / a.H], 0), T) : T;
   const int nchunks = (Tb + kChunk - 1) / kChunk;
   const int my_row = row0 + n;
+  // this wave's output tiles TW w .. TW w + TW - 1, in contraction block ob (with
+  // TW = 1, half hw of it)
+  const int ob = TW * w / 2, hw = TW == 1 ? w % 2 : 0;
 
   unsigned short* xb = reinterpret_cast<unsigned short*>(lds + L::XB_OFF);
   unsigned short* xl = reinterpret_cast<unsigned short*>(lds + L::XL_OFF);
@@ -276,7 +289,7 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   const unsigned int* zero_lds = reinterpret_cast<const unsigned int*>(lds + L::Z_OFF);
 
   // ---- prologue: chunk 0/1 inputs, W, H0 requested before the first wait
-  LongStager<V, GRID, F16> st, st1;
+  LongStager<V, GRID, F16, TW> st, st1;
   st.load(a, unit, row0, 0, Tb, LD);
   if (nchunks > 1) st1.load(a, unit, row0, 1, Tb, LD);
   constexpr int WLOADS = V * V / 8 / L::THREADS;
@@ -309,26 +322,26 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
     for (int off = 32; off >= 1; off /= 2) hmax = fmaxf(hmax, __shfl_xor(hmax, off));
     if (l == 0) ybt[w] = hmax;  // read after the W-staging barrier below
   }
-  f4 G[2];  // own output tiles 2w, 2w + 1: lane (g, n) holds G[n][16 c + 4 g + i]
+  f4 G[TW];  // own output tiles TW w + j: lane (g, n) holds G[n][16 c + 4 g + i]
   {
     const float* H0 = a.H0 ? a.H0 + (unit * a.K + my_row) * V : nullptr;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      G[j] = H0 ? *reinterpret_cast<const f4*>(H0 + 16 * (2 * w + j) + 4 * g) * kC : f4{0, 0, 0, 0};
+    for (int j = 0; j < TW; ++j)
+      G[j] = H0 ? *reinterpret_cast<const f4*>(H0 + 16 * (TW * w + j) + 4 * g) * kC : f4{0, 0, 0, 0};
     if constexpr (F16) {
       // an initial state beyond the fp16 operand's range is NaN from the start;
       // with gates in [0, 1] the state never grows past max(1, max |H0|) after it
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TW; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) G[j][i] = f16_range_or_nan(G[j][i]);
     }
   }
-  // W^T fragments of this wave's two output tiles, every contraction block, via
+  // W^T fragments of this wave's output tiles, every contraction block, via
   // LDS. Register arrays over the blocks are indexed o = 0 .. KB - 1 for block
-  // (w + o) mod KB (o = 0: the wave's own block), so that every register index
+  // (ob + o) mod KB (o = 0: the wave's own block), so that every register index
   // is a compile-time constant; only LDS addresses depend on the wave.
-  Op Wf[2][KB];
+  Op Wf[TW][KB];
   {
     unsigned short* wst = reinterpret_cast<unsigned short*>(lds + L::VX_OFF);
 #pragma unroll
@@ -340,10 +353,10 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
     if constexpr (GRID)
       for (int ww = 0; ww < L::S; ++ww) hmax = fmaxf(hmax, ybt[ww]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TW; ++j)
 #pragma unroll
       for (int o = 0; o < KB; ++o) {
-        const int c = 2 * w + j, b = (w + o) % KB;
+        const int c = TW * w + j, b = (ob + o) % KB;
         const unsigned short* src = wst + (32 * b + 4 * g + n / 4) * HROW + 16 * c + 4 * (n % 4);
         const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)src);
         const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * HROW));
@@ -368,12 +381,14 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   if (nchunks > 2) st.load(a, unit, row0, 2, Tb, LD);
 
   // operand blocks: Bf[o] lane (g, n) = bf16 G[n][32 b + 16 (j / 4) + 4 g + j % 4],
-  // b = (w + o) mod KB
+  // b = (ob + o) mod KB. With TW = 1 the wave makes half of its own block (its
+  // tile's four elements, in the other half zeros that are never stored) and
+  // reads every block, its own included, back after the exchange.
   Op Bf[KB], Bl[KB];
   auto make_own = [&]() {
     f8 x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { x[i] = G[0][i]; x[4 + i] = G[1][i]; }
+    for (int i = 0; i < 4; ++i) { x[i] = G[0][i]; x[4 + i] = TW == 2 ? G[TW - 1][i] : 0.0f; }
     Bf[0] = __builtin_convertvector(x, Op);
     if constexpr (SPLIT) {
       const u4 hb = __builtin_bit_cast(u4, Bf[0]);
@@ -388,19 +403,26 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   };
   // the shared state tile slot of step s: row n, block b at columns 32 b + 8 g
   auto publish_own = [&](int slot) {
-    *reinterpret_cast<Op*>(xb + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bf[0];
-    if constexpr (SPLIT) *reinterpret_cast<Op*>(xl + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bl[0];
+    if constexpr (TW == 2) {
+      *reinterpret_cast<Op*>(xb + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bf[0];
+      if constexpr (SPLIT) *reinterpret_cast<Op*>(xl + slot * 16 * HROW + n * HROW + 32 * w + 8 * g) = Bl[0];
+    } else {
+      // the tile's four elements: half hw of the block's fragment
+      const int off = slot * 16 * HROW + n * HROW + 32 * ob + 8 * g + 4 * hw;
+      *reinterpret_cast<u2*>(xb + off) = __builtin_bit_cast(u4, Bf[0]).xy;
+      if constexpr (SPLIT) *reinterpret_cast<u2*>(xl + off) = __builtin_bit_cast(u4, Bl[0]).xy;
+    }
   };
   auto fetch_others = [&](int slot) {
 #pragma unroll
-    for (int o = 1; o < KB; ++o) {
-      const int b = (w + o) % KB;
+    for (int o = TW == 2 ? 1 : 0; o < KB; ++o) {
+      const int b = (ob + o) % KB;
       Bf[o] = *reinterpret_cast<const Op*>(xb + slot * 16 * HROW + n * HROW + 32 * b + 8 * g);
       if constexpr (SPLIT) Bl[o] = *reinterpret_cast<const Op*>(xl + slot * 16 * HROW + n * HROW + 32 * b + 8 * g);
     }
   };
-  // rank-1 term of step s of the chunk in stage buffer sb: acc[j] = (v, tile 2w + j) x (hi, lo of c k)
-  auto rank1 = [&](int sb, int s, f4 (&acc)[2]) {
+  // rank-1 term of step s of the chunk in stage buffer sb: acc[j] = (v, tile TW w + j) x (hi, lo of c k)
+  auto rank1 = [&](int sb, int s, f4 (&acc)[TW]) {
     const unsigned int* kx = kx_all + sb * kChunk * 16;
     const unsigned int* vx = vx_all + sb * kChunk * 16 * L::NVX;
     const unsigned int kp = *((g == 0) ? kx + s * 16 + n : zero_lds);
@@ -410,28 +432,37 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
     // its accumulator a few instructions later read it before the result was
     // there, and here the compiler places the rank-1 write within a few
     // instructions of the first product into the same accumulator.
-    const uint2 win = *reinterpret_cast<const uint2*>(vx + (s * 16 + n) * L::NVX + 2 * w);
-    const bf16x8 av = __builtin_bit_cast(bf16x8, u4{win.x, win.y, 0u, 0u});
-    acc[0] = mfma(av, __builtin_bit_cast(bf16x8, u4{kp, 0u, 0u, 0u}), f4{0, 0, 0, 0});
-    acc[1] = mfma(av, __builtin_bit_cast(bf16x8, u4{0u, kp, 0u, 0u}), f4{0, 0, 0, 0});
+    if constexpr (TW == 2) {
+      const uint2 win = *reinterpret_cast<const uint2*>(vx + (s * 16 + n) * L::NVX + 2 * w);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, u4{win.x, win.y, 0u, 0u});
+      acc[0] = mfma(av, __builtin_bit_cast(bf16x8, u4{kp, 0u, 0u, 0u}), f4{0, 0, 0, 0});
+      acc[TW - 1] = mfma(av, __builtin_bit_cast(bf16x8, u4{0u, kp, 0u, 0u}), f4{0, 0, 0, 0});
+    } else {
+      const unsigned int win = vx[(s * 16 + n) * L::NVX + w];
+      acc[0] = mfma(__builtin_bit_cast(bf16x8, u4{win, 0u, 0u, 0u}), __builtin_bit_cast(bf16x8, u4{kp, 0u, 0u, 0u}),
+                    f4{0, 0, 0, 0});
+    }
   };
-  auto products = [&](int o, f4 (&acc)[2]) {
+  auto products = [&](int o, f4 (&acc)[TW]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TW; ++j) {
       acc[j] = mfma(Wf[j][o], Bf[o], acc[j]);
       if constexpr (SPLIT) acc[j] = mfma(Wf[j][o], Bl[o], acc[j]);
     }
   };
 
-  // readout partials: Dr[j] lane (g, n) accumulates y_{t0 + n}[position 16 (2w + j) + 4 g + i]
-  // over the tile's 16 rows (positions are the permuted order of the state tiles)
-  f4 Dr[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
+  // readout partials: Dr[j] lane (g, n) accumulates y_{t0 + n}[position 16 (TW w + j) + 4 g + i]
+  // over the tile's 16 rows (positions are the permuted order of the state tiles:
+  // position 32 b + 8 g' + e holds column 32 b + 16 (e / 4) + 4 g' + e % 4)
+  f4 Dr[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) Dr[j] = f4{0, 0, 0, 0};
   // in two parts, so that the LDS reads go out with the exchange's and the
   // MFMAs follow the step's products
   // with SPLIT the low halves of the state are read out too (their tiles are
   // exchanged anyway), so y carries the split operand's precision
   struct ReadoutOps {
-    Op q, s[2], sl[SPLIT ? 2 : 1];
+    Op q, s[TW], sl[SPLIT ? TW : 1];
   };
   auto readout_load = [&](int sb, int s0, int nvalid) {
     ReadoutOps r;
@@ -441,8 +472,8 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
     r.q = __builtin_bit_cast(Op, qv);
     const unsigned short* src = xb + (s & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int P = 2 * w + j;
+    for (int j = 0; j < TW; ++j) {
+      const int P = TW * w + j;
       const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(src + 16 * P));
       const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s4*)(src + 16 * P + 4 * HROW));
@@ -459,7 +490,7 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   };
   auto readout_mma = [&](const ReadoutOps& r) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TW; ++j) {
       Dr[j] = mfma(r.s[j], r.q, Dr[j]);
       if constexpr (SPLIT) Dr[j] = mfma(r.sl[j], r.q, Dr[j]);
     }
@@ -468,7 +499,7 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   // A chunk's sums are added at step 1 of the next chunk, after that step's
   // staging: the staging waits for all of the wave's outstanding global
   // operations, and by then the adds are 15 steps old instead of one.
-  f4 Dp[2];
+  f4 Dp[TW];
   int pend_t0 = 0, pend_n = 0;
   float* ys = reinterpret_cast<float*>(lds + L::YS_OFF) + w * 16 * L::YS_ROW;
   auto add_y = [&]() {
@@ -483,26 +514,33 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
       // operand: 2^E > 1.0625 ||q_t||_1 M
       const float* ybp = ybt + ((pend_t0 / kChunk) & (L::YB_SLOTS - 1)) * L::YB_PER;
       const int e = GRID ? __builtin_amdgcn_frexp_expf(ybp[n] * ybp[kChunk] * 1.0625f) : 0;
+      // (local column within block ob: 16 (g % 2) + 8 j' + 4 (g / 2) + i, j' the
+      // tile's half of the block)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TW; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float x = Dp[j][i] * kInvC;
           if constexpr (GRID) x = __builtin_amdgcn_ldexpf(__builtin_rintf(__builtin_amdgcn_ldexpf(x, 23 - e)), e - 23);
-          ys[n * L::YS_ROW + 16 * (g % 2) + 8 * j + 4 * (g / 2) + i] = x;
+          ys[n * L::YS_ROW + 16 * (g % 2) + 8 * (TW == 2 ? j : hw) + 4 * (g / 2) + i] = x;
         }
       __builtin_amdgcn_wave_barrier();
       // every value first, then the adds with no branch between them: a row
       // past the sequence's end adds zero to the chunk's last valid row (x + 0
-      // is x), so the adds need no predicate and the reads one wait
-      float val[8];
+      // is x), so the adds need no predicate and the reads one wait. Each add
+      // instruction covers 64 / (16 TW) rows of 16 TW floats of the wave's
+      // columns (TW = 1: local columns 8 hw .. +7 and 16 + 8 hw .. +7)
+      constexpr int LPR = 16 * TW, NV = 4 * TW;
+      const int k = l % LPR;
+      const int lc = TW == 2 ? k : 8 * hw + k + 8 * (k / 8);
+      float val[NV];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) val[r] = ys[(2 * r + l / 32) * L::YS_ROW + l % 32];
+      for (int r = 0; r < NV; ++r) val[r] = ys[((64 / LPR) * r + l / LPR) * L::YS_ROW + lc];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int row = 2 * r + l / 32;
+      for (int r = 0; r < NV; ++r) {
+        const int row = (64 / LPR) * r + l / LPR;
         const bool live = row < pend_n;
-        unsafeAtomicAdd(a.y + (unit * LD + pend_t0 + (live ? row : pend_n - 1)) * V + 32 * w + l % 32,
+        unsafeAtomicAdd(a.y + (unit * LD + pend_t0 + (live ? row : pend_n - 1)) * V + 32 * ob + lc,
                         live ? val[r] : 0.0f);
       }
     }
@@ -521,7 +559,7 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
   publish_own(NHS - 1);
   lds_barrier();  // staged chunks, W-region reuse, and the operand blocks are visible
   fetch_others(NHS - 1);
-  f4 acc[2];
+  f4 acc[TW];
   f4 gate = *reinterpret_cast<const f4*>(fs_all);  // step 0's gate scalars
   if (nchunks > 0) {
     rank1(0, 0, acc);
@@ -544,18 +582,18 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
       // the next step's rank-1 term goes first, into its own accumulators: it
       // needs only staged inputs, and the matrix cores and LDS are otherwise
       // idle during the epilogue
-      f4 accn[2];
+      f4 accn[TW];
       if constexpr (s + 1 < kChunk) rank1(sb, s + 1, accn); else rank1(sb ^ 1, 0, accn);
-      // acc holds c (G_{t-1} W + k_t v_t^T) for this wave's two tiles
+      // acc holds c (G_{t-1} W + k_t v_t^T) for this wave's tiles
       [[maybe_unused]] const int t = c * kChunk + s;
       if constexpr (SAVE) {
         if (t < Tb)
           *reinterpret_cast<u4*>(saved + saved_pre_off(unit, t, a.B, a.H, T, a.K, V) + sv_off) =
-              u4{pack_bf16(acc[0][0], acc[0][1]), pack_bf16(acc[0][2], acc[0][3]), pack_bf16(acc[1][0], acc[1][1]),
-                 pack_bf16(acc[1][2], acc[1][3])};
+              u4{pack_bf16(acc[0][0], acc[0][1]), pack_bf16(acc[0][2], acc[0][3]),
+                 pack_bf16(acc[TW - 1][0], acc[TW - 1][1]), pack_bf16(acc[TW - 1][2], acc[TW - 1][3])};
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TW; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e = __builtin_amdgcn_exp2f(acc[j][i]);
@@ -567,7 +605,7 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
         if (t < Tb) *reinterpret_cast<bf16x8*>(saved + saved_state_off(unit, t + 1, T, a.K, V) + sv_off) = Bf[0];
       }
       publish_own(s & (NHS - 1));
-      products(0, accn);
+      if constexpr (TW == 2) products(0, accn);  // the own block is whole in registers
       lds_barrier();
       gate = *reinterpret_cast<const f4*>((s + 1 < kChunk ? fsb : fsn) + 4 * ((s + 1) % kChunk));
       ReadoutOps ro;
@@ -577,14 +615,14 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
       // blocks (twice as many MFMAs when split) still run, and the next step's
       // epilogue of tile 0 issues under them
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TW; ++j)
 #pragma unroll
-        for (int o = 1; o < KB; ++o) {
+        for (int o = TW == 2 ? 1 : 0; o < KB; ++o) {
           accn[j] = mfma(Wf[j][o], Bf[o], accn[j]);
           if constexpr (SPLIT) accn[j] = mfma(Wf[j][o], Bl[o], accn[j]);
         }
-      acc[0] = accn[0];
-      acc[1] = accn[1];
+#pragma unroll
+      for (int j = 0; j < TW; ++j) acc[j] = accn[j];
       if constexpr ((s & 1) != 0) readout_mma(ro);
       if constexpr (s == 1) {
         // chunks 0 and 1 were staged before the loop; from chunk 1 on, step 1
@@ -597,22 +635,23 @@ __global__ __launch_bounds__(64 * (V / 32), 1) void mfma_fwd_long_kernel(FwdArgs
         add_y();  // chunk c - 1's sums
       }
     });
-    Dp[0] = Dr[0];
-    Dp[1] = Dr[1];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      Dp[j] = Dr[j];
+      Dr[j] = f4{0, 0, 0, 0};
+    }
     pend_t0 = c * kChunk;
     pend_n = ns;
-    Dr[0] = f4{0, 0, 0, 0};
-    Dr[1] = f4{0, 0, 0, 0};
   }
   add_y();  // the last chunk's sums
   // H_T: the state after step Tb (H0 itself for an empty sequence)
   if (a.HT) {
     float* HT = a.HT + (unit * a.K + my_row) * V;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TW; ++j) {
       f4 x = G[j] * kInvC;
-      if (nchunks == 0 && a.H0) x = *reinterpret_cast<const f4*>(a.H0 + (unit * a.K + my_row) * V + 16 * (2 * w + j) + 4 * g);
-      *reinterpret_cast<f4*>(HT + 16 * (2 * w + j) + 4 * g) = x;
+      if (nchunks == 0 && a.H0) x = *reinterpret_cast<const f4*>(a.H0 + (unit * a.K + my_row) * V + 16 * (TW * w + j) + 4 * g);
+      *reinterpret_cast<f4*>(HT + 16 * (TW * w + j) + 4 * g) = x;
     }
   }
 }
@@ -623,10 +662,17 @@ bool long_supports(const FwdArgs& a) {
   return a.bf16 && (a.V == 64 || a.V == 128) && a.K % 16 == 0 && a.K >= 16 && a.K <= 128;
 }
 
+// Output tiles per wave of the plain forward (the saving forward always takes
+// two). At V = 64 one tile per wave (four waves per 16-row tile) runs a step in
+// 0.77x the time of two (B=4 H=8 K=V=64 T=512: 0.139 against 0.181 ms, fp16
+// operand); at V = 128 eight waves per tile are no faster than four (C4 and C5
+// within +-2 % single operand, 6 % slower split), so it keeps two.
+constexpr int long_tw(int V) { return V == 64 ? 1 : 2; }
+
 Plan plan_long(int B, int H, int K, int V) {
   const long long grid = (long long)B * H * (K / 16);
-  return Plan{grid > 0x7fffffffLL ? -1 : (int)grid, 64 * (V / 32), 16, K / 16, 1,
-              V == 128 ? LongLayout<128, true>::TOTAL : LongLayout<64, true>::TOTAL};
+  return Plan{grid > 0x7fffffffLL ? -1 : (int)grid, 64 * V / (16 * long_tw(V)), 16, K / 16, 1,
+              V == 128 ? LongLayout<128, true, long_tw(128)>::TOTAL : LongLayout<64, true, long_tw(64)>::TOTAL};
 }
 
 hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream, bool f16) {
@@ -638,14 +684,16 @@ hipError_t launch_long(const FwdArgs& a, bool split, hipStream_t stream, bool f1
     hipError_t e = fill_zero(a.y, (long long)a.B * a.H * a.T * a.V, stream);
     if (e != hipSuccess) return e;
   }
-  const dim3 block(64 * (a.V / 32)), gr((unsigned)grid);
   const bool save = a.saved != nullptr;
-#define M2RNN_LONG_LAUNCH(V_, S_, SV_) hipLaunchKernelGGL((mfma_fwd_long_kernel<V_, S_, SV_, false>), gr, block, 0, stream, a)
+  // (the saving forward: two tiles per wave; the plain one: long_tw(V))
+  const dim3 block(64 * a.V / (16 * (save ? 2 : long_tw(a.V)))), gr((unsigned)grid);
+#define M2RNN_LONG_LAUNCH(V_, S_, SV_) \
+  hipLaunchKernelGGL((mfma_fwd_long_kernel<V_, S_, SV_, false, SV_ ? 2 : long_tw(V_)>), gr, block, 0, stream, a)
   if (f16) {
     if (a.V == 128)
-      hipLaunchKernelGGL((mfma_fwd_long_kernel<128, false, false, true>), gr, block, 0, stream, a);
+      hipLaunchKernelGGL((mfma_fwd_long_kernel<128, false, false, true, long_tw(128)>), gr, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((mfma_fwd_long_kernel<64, false, false, true>), gr, block, 0, stream, a);
+      hipLaunchKernelGGL((mfma_fwd_long_kernel<64, false, false, true, long_tw(64)>), gr, block, 0, stream, a);
   } else if (a.V == 128) {
     if (split) {
       if (save) M2RNN_LONG_LAUNCH(128, true, true); else M2RNN_LONG_LAUNCH(128, true, false);

@@ -86,7 +86,8 @@ def test_final_state_is_bitwise_repeatable():
     assert np.array_equal(y0, y1)  # grid-rounded row-tile sums: order-independent
 
 
-def test_ragged_lengths_and_accumulate():
+@pytest.mark.parametrize("algo", ["mfma_long_split", "mfma_long_f16"])
+def test_ragged_lengths_and_accumulate(algo):
     import torch
     from non_linear_matrix_amd import m2rnn
     from oracle import m2rnn_fwd_ref
@@ -94,13 +95,13 @@ def test_ragged_lengths_and_accumulate():
     T = 37
     lens = [37, 0, 1, 16, 17, 30]
     cfg = scaled(CONFIGS["C3"], B=len(lens), H=2, T=T, K=64)
-    announce(f"long varlen lens={lens}")
+    announce(f"long varlen lens={lens} {algo}")
     x = generate(cfg, 64)
     d = to_device(x)
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     base = torch.full((cfg.B, cfg.H, T, cfg.V), 0.25, device="cuda")
     y = base.clone()
-    _, HT = m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], y=y, seq_len=sl, algo="mfma_long_split",
+    _, HT = m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], y=y, seq_len=sl, algo=algo,
                       accumulate_y=True)
     torch.cuda.synchronize()
     yd = (y - base).cpu().numpy()
@@ -181,19 +182,20 @@ def test_default_forward_is_bitwise_repeatable(name):
         assert np.array_equal(y1, y2) and np.array_equal(H1, H2)
 
 
-def test_graph_replays():
+@pytest.mark.parametrize("algo", ["mfma_long_split", "mfma_long_f16"])
+def test_graph_replays(algo):
     """Captured in a HIP graph (y cleared by a fill kernel): every replay gives
     the eager H_T bit for bit and y to rounding."""
     import torch
     from non_linear_matrix_amd import m2rnn
 
     cfg = scaled(CONFIGS["C3"], B=1, H=2, K=64, T=40)
-    announce("long kernel graph replay")
+    announce(f"long kernel graph replay, {algo}")
     d = to_device(generate(cfg, 67))
-    y_e, HT_e = m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], algo="mfma_long_split")
+    y_e, HT_e = m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], algo=algo)
     torch.cuda.synchronize()
     y, HT = torch.empty_like(y_e), torch.empty_like(HT_e)
-    fn = lambda: m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], y=y, H_T=HT, algo="mfma_long_split")
+    fn = lambda: m2rnn.fwd(d["k"], d["v"], d["q"], d["f"], d["W"], d["H0"], y=y, H_T=HT, algo=algo)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):

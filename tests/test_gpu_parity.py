@@ -149,7 +149,8 @@ def test_gate_one_keeps_state(algo):
     assert nerr(y, yr) <= _tol(cfg, algo)
 
 
-@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split", "mfma_long", "mfma_long_split"])
+@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split", "mfma_long", "mfma_long_split", "mfma_f16",
+                                  "mfma_long_f16"])
 def test_deterministic(algo):
     cfg = scaled(CONFIGS["C3"], B=2, H=4, T=64)
     x = generate(cfg, 7)
@@ -159,7 +160,8 @@ def test_deterministic(algo):
     assert np.array_equal(y1, y2) and np.array_equal(HT1, HT2)
 
 
-@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split", "mfma_long", "mfma_long_split"])
+@pytest.mark.parametrize("algo", ["simple", "mfma", "mfma_split", "mfma_long", "mfma_long_split", "mfma_f16",
+                                  "mfma_long_f16"])
 def test_chunked_continuation(algo):
     """fwd(T1) then fwd(T2, H0 = H_T) continues fwd(T1 + T2): bitwise for the fp32
     kernel. The matrix-core kernels carry c H (c = 2 / ln 2) and hand back
