@@ -560,7 +560,15 @@ __global__ __launch_bounds__(64 * V / (16 * TW), 1) void mfma_fwd_long_kernel(Fw
   lds_barrier();  // staged chunks, W-region reuse, and the operand blocks are visible
   fetch_others(NHS - 1);
   f4 acc[TW];
-  f4 gate = *reinterpret_cast<const f4*>(fs_all);  // step 0's gate scalars
+  // a step's gate scalars (f, a, -2 a) from its 16-byte record: only the three
+  // used components are loaded, so the allocator cannot reuse the fourth's
+  // register while the load is in flight (which forced a wait for the load
+  // before the exchange reads could go out)
+  auto gate_at = [](const float* p) {
+    const float2 fa = *reinterpret_cast<const float2*>(p);
+    return f4{fa.x, fa.y, p[2], 0.0f};
+  };
+  f4 gate = gate_at(fs_all);  // step 0's gate scalars
   if (nchunks > 0) {
     rank1(0, 0, acc);
 #pragma unroll
@@ -607,7 +615,7 @@ __global__ __launch_bounds__(64 * V / (16 * TW), 1) void mfma_fwd_long_kernel(Fw
       publish_own(s & (NHS - 1));
       if constexpr (TW == 2) products(0, accn);  // the own block is whole in registers
       lds_barrier();
-      gate = *reinterpret_cast<const f4*>((s + 1 < kChunk ? fsb : fsn) + 4 * ((s + 1) % kChunk));
+      gate = gate_at((s + 1 < kChunk ? fsb : fsn) + 4 * ((s + 1) % kChunk));
       ReadoutOps ro;
       if constexpr ((s & 1) != 0) ro = readout_load(sb, s - 1, 2);
       fetch_others(s & (NHS - 1));

@@ -41,7 +41,10 @@
 // With SPLIT the operand is the pair hi = bf16(G), lo = bf16(G - hi) (the
 // residual is exact in fp32) and every product takes two passes, W hi + W lo:
 // ~16 significant bits instead of 8 for trajectories that amplify per-step
-// rounding (W is a bf16 input, so it is exact either way).
+// rounding (W is a bf16 input, so it is exact either way). With F16 the single
+// operand is fp16 instead (11 significant bits, the same MFMA rate and layout on
+// v_mfma_f32_16x16x32_f16; W and q converted once, exactly inside fp16's range,
+// and a value beyond that range turned into NaN).
 //
 // Readout. Each wave writes its rounded state tile to its own LDS slot and,
 // every second step, reads the two tiles back transposed with
@@ -471,15 +474,23 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     // threads add into consecutive floats and each add instruction covers whole
     // 128-byte rows of y (with four consecutive floats per lane each 4-byte add
     // rewrote a 16-byte piece of memory: 3.9x the HBM writes at C3)
+    // (every partial is read before the first add, so the reads share one wait
+    // instead of one LDS round trip per column)
     float* dst = y + (unit * LD + t0 + sn) * V;
+    float part[4][NW];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int col = j + (V / 4) * i, r = col % 32;
       const int pos = 16 * (2 * (col / 32) + (r % 16) / 8) + 4 * (2 * ((r % 8) / 4) + r / 16) + r % 4;
-      float sum = ypb[sn * L::YROW + pos];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) sum += ypb[(ww * kChunk + sn) * L::YROW + pos];
-      unsafeAtomicAdd(dst + col, sum * kInvC);
+      for (int ww = 0; ww < NW; ++ww) part[i][ww] = ypb[(ww * kChunk + sn) * L::YROW + pos];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sum = part[i][0];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) sum += part[i][ww];
+      unsafeAtomicAdd(dst + j + (V / 4) * i, sum * kInvC);
     }
   };
 
