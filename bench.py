@@ -38,14 +38,14 @@ METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
     # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
-    ("C3", "mfma_f16"): (136565.0, 270336.0, "m2rnn_mfma.hip",
-                         "0436cbb1844c14948cf1a80575cee4dd920a6a24bc5cc080a2ef9585a0b554dd"),
+    ("C3", "mfma_f16"): (136562.3, 270336.0, "m2rnn_mfma.hip",
+                         "8ad3ab716ad256ed4dc0bae60f0b05f81565999d116e9e16fc7f9d6bc6c71b8e"),
     ("D1", "decode"): (267349.0, 528389.4, "m2rnn_decode.hip",
                        "d6f09bfc7c21aa0dc4fc5e513ca60a152b47059c85446459709af8e502678a47"),
-    ("C4", "mfma_long_f16"): (669879.6, 1050624.0, "m2rnn_long.hip",
-                              "77f5455b82cd955bb1e03536c2bd0ee2ca06053b2522b09b376819a89569f855"),
-    ("C5", "mfma_long_f16"): (1053879.0, 2098176.0, "m2rnn_long.hip",
-                              "77f5455b82cd955bb1e03536c2bd0ee2ca06053b2522b09b376819a89569f855"),
+    ("C4", "mfma_long_f16"): (669878.6, 1050624.0, "m2rnn_long.hip",
+                              "c63c1b2986b8690e7e10cdd7ba8d810acc1b26ee1f75922255741238322b2c14"),
+    ("C5", "mfma_long_f16"): (1053878.1, 2098176.0, "m2rnn_long.hip",
+                              "c63c1b2986b8690e7e10cdd7ba8d810acc1b26ee1f75922255741238322b2c14"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the
