@@ -264,3 +264,20 @@ def test_recompute_mode_on_the_long_kernel():
     assert nerr(y.cpu().numpy(), ref["y"]) <= TOL and nerr(HT.cpu().numpy(), ref["H_T"]) <= TOL
     for key in ("dk", "dv", "dq", "df", "dW", "dH0"):
         assert nerr(g[key].cpu().numpy(), ref[key]) <= TOL, key
+
+
+@pytest.mark.parametrize("algo", ["mfma_long_f16", "mfma_long_split", "mfma_long"])
+def test_more_row_tiles_than_cus(algo):
+    """More 16-row tiles than the GPU has CUs (3 x 16 x 128 rows: 384 tiles, two
+    workgroups on some CUs), every unit against the oracle."""
+    from non_linear_matrix_amd import m2rnn
+    cfg = scaled(CONFIGS["C3"], B=3, H=16, K=128, T=37)
+    p = m2rnn.get_plan(cfg.B, cfg.H, cfg.T, cfg.K, cfg.V, cfg.dtype, algo)
+    assert p["rows_per_group"] == 16 and p["grid"] == 384
+    announce(f"long kernel, 16-row tiles, {algo}")
+    x = generate(cfg, 70)
+    yr, HTr = oracle_units(x, cfg.dtype)
+    y, HT = gpu_run(x, algo=algo)
+    ey, eh = nerr(y, yr), nerr(HT, HTr)
+    print(f"{algo} 384 tiles: y {ey:.2e} H_T {eh:.2e}", flush=True)
+    assert ey <= TOL and eh <= TOL
