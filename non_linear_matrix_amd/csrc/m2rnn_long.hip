@@ -467,8 +467,19 @@ __global__ __launch_bounds__(64 * V / (16 * TW), 1) void mfma_fwd_long_kernel(Fw
   auto readout_load = [&](int sb, int s0, int nvalid) {
     ReadoutOps r;
     const int p = g / 2, rr = 8 * (g % 2), s = s0 + p;
-    s8 qv = *reinterpret_cast<const s8*>(qs_all + sb * kChunk * 16 + s * 16 + rr);
-    if (n != s || p >= nvalid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
+    // (q_s in column s of the operand, zero elsewhere). With two tiles per wave
+    // every lane loads and the others' q is masked to zero afterwards: the load
+    // under a lane condition compiled into a branch around it, 1-1.6 % of C4 and
+    // C5; with one tile per wave (V = 64) the branch measured faster (C2 1-4 %).
+    const u4* qsrc = reinterpret_cast<const u4*>(qs_all + sb * kChunk * 16 + s * 16 + rr);
+    const bool use = n == s && p < nvalid;
+    u4 qv;
+    if constexpr (TW == 2) {
+      qv = *qsrc & (use ? ~0u : 0u);
+    } else {
+      qv = u4{0, 0, 0, 0};
+      if (use) qv = *qsrc;
+    }
     r.q = __builtin_bit_cast(Op, qv);
     const unsigned short* src = xb + (s & (NHS - 1)) * 16 * HROW + (rr + n / 4) * HROW + 4 * (n % 4);
 #pragma unroll
