@@ -42,10 +42,10 @@ TRAFFIC_KIB = {
                          "8ad3ab716ad256ed4dc0bae60f0b05f81565999d116e9e16fc7f9d6bc6c71b8e"),
     ("D1", "decode"): (267349.0, 528389.4, "m2rnn_decode.hip",
                        "d6f09bfc7c21aa0dc4fc5e513ca60a152b47059c85446459709af8e502678a47"),
-    ("C4", "mfma_long_f16"): (669878.6, 1050624.0, "m2rnn_long.hip",
-                              "c63c1b2986b8690e7e10cdd7ba8d810acc1b26ee1f75922255741238322b2c14"),
-    ("C5", "mfma_long_f16"): (1053878.1, 2098176.0, "m2rnn_long.hip",
-                              "c63c1b2986b8690e7e10cdd7ba8d810acc1b26ee1f75922255741238322b2c14"),
+    ("C4", "mfma_long_f16"): (669879.5, 1050624.0, "m2rnn_long.hip",
+                              "044752d9671f142c0c248f310f8d9d597aba91fc478870a0af20264645e9a3f1"),
+    ("C5", "mfma_long_f16"): (1053879.0, 2098176.0, "m2rnn_long.hip",
+                              "044752d9671f142c0c248f310f8d9d597aba91fc478870a0af20264645e9a3f1"),
 }
 CSRC = os.path.join(ROOT, "non_linear_matrix_amd", "csrc")
 # the save-mode backward call on C3 (reverse kernel + dW partials + dW reduce), the
