@@ -38,8 +38,8 @@ METRIC = "M2RNN fwd tokens·heads/sec + MFMA util % at K=V=128, 1×MI355X"
 COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC_KIB = {
     # (workload, algo): (FETCH_SIZE KiB, WRITE_SIZE KiB, kernel source, its sha256)
-    ("C3", "mfma_f16"): (136562.3, 270336.0, "m2rnn_mfma.hip",
-                         "8ad3ab716ad256ed4dc0bae60f0b05f81565999d116e9e16fc7f9d6bc6c71b8e"),
+    ("C3", "mfma_f16"): (136562.8, 270336.0, "m2rnn_mfma.hip",
+                         "c0221ee00f30a9a0fcd443891b9b410f7f841bd197bebde88055a087d4980c0c"),
     ("D1", "decode"): (267349.0, 528389.4, "m2rnn_decode.hip",
                        "d6f09bfc7c21aa0dc4fc5e513ca60a152b47059c85446459709af8e502678a47"),
     ("C4", "mfma_long_f16"): (669879.5, 1050624.0, "m2rnn_long.hip",

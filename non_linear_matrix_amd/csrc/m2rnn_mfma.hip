@@ -407,9 +407,19 @@ __global__ __launch_bounds__(64 * NW, 1) void mfma_fwd_kernel(FwdArgs a) {
     const int p = g / 2;                 // which step of the pair this lane group carries
     const int rr = 8 * (g % 2);          // first of its 8 rows
     const int s = s0 + p;
-    s8 qv = *reinterpret_cast<const s8*>(B.qs + s * R + 16 * w + rr);
-    if (n != s || p >= nvalid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
-    return __builtin_bit_cast(Op, qv);  // q_{s0 + p} in column s0 + p (p < nvalid), zero elsewhere
+    // q_{s0 + p} in column s0 + p (p < nvalid), zero elsewhere. With the split
+    // operand every lane loads and the lanes of other columns mask their q to
+    // zero (1.2 % faster on C3 than the load under a lane condition, which
+    // compiles into exec-mask changes); with one operand the conditional load
+    // measured 0.4-0.8 % faster.
+    if constexpr (SPLIT) {
+      const u4 qv = *reinterpret_cast<const u4*>(B.qs + s * R + 16 * w + rr) & ((n != s || p >= nvalid) ? 0u : ~0u);
+      return __builtin_bit_cast(Op, qv);
+    } else {
+      s8 qv = *reinterpret_cast<const s8*>(B.qs + s * R + 16 * w + rr);
+      if (n != s || p >= nvalid) qv = s8{0, 0, 0, 0, 0, 0, 0, 0};
+      return __builtin_bit_cast(Op, qv);
+    }
   };
   auto readout_load = [&](int s0, int half) {
     RO ro;
