@@ -574,10 +574,13 @@ def main():
     hbm_gbs = algo_bytes / (kern_avg * 1e-3) / 1e9
     # the other matrix-core variant on the same workload, for reference (not `value`)
     alt = None
-    others = {"mfma": "mfma_split", "mfma_split": "mfma", "mfma_long": "mfma_long_split",
-              "mfma_long_split": "mfma_long", "mfma_f16": "mfma_split", "mfma_long_f16": "mfma_long_split"}
-    if args.algo in others and cfg.T > 1:
-        other = others[args.algo]
+    # the other operand variants of the same kernel family on the same workload,
+    # timed for reference (never `value`)
+    others = {"mfma": ["mfma_split"], "mfma_split": ["mfma"], "mfma_long": ["mfma_long_split"],
+              "mfma_long_split": ["mfma_long"], "mfma_f16": ["mfma_split", "mfma"],
+              "mfma_long_f16": ["mfma_long_split", "mfma_long"]}
+    alts = []
+    for other in (others.get(args.algo, []) if cfg.T > 1 else []):
         def alt_step():
             if clear_here:
                 y.zero_()
@@ -594,8 +597,9 @@ def main():
         a1.record(stream)
         torch.cuda.synchronize()
         alt_ms = a0.elapsed_time(a1) / n_alt
-        alt = {"algo": other, "ms_per_step": alt_ms, "tok_heads_per_s": tokens / (alt_ms * 1e-3),
-               "note": "the other operand variant of the same kernel family; not the headline value"}
+        alts.append({"algo": other, "ms_per_step": alt_ms, "tok_heads_per_s": tokens / (alt_ms * 1e-3),
+                     "note": "another operand variant of the same kernel family; not the headline value"})
+    alt = alts[0] if alts else None
     out = {
         "metric": METRIC,
         "value": value,
@@ -638,6 +642,7 @@ def main():
         },
         "hbm_GBps_algorithmic": hbm_gbs,
         "other_variant": alt,
+        "other_variants": alts,
         "settle": {"calls": settle_calls, "min_ms": SETTLE_MS,
                    "note": "untimed steps before the warmup, until the clock has settled"},
         "wall_s": wall,
