@@ -227,8 +227,9 @@ unsigned long long m2rnn_saved_bytes(int B, int H, int T, int K, int V);
 /* Training forward: m2rnn_fwd_algo that also fills `saved` (device, 16-byte
  * aligned, m2rnn_saved_bytes large, caller-owned; its layout is private to the
  * library and only m2rnn_bwd reads it). algo: MFMA, MFMA_SPLIT, MFMA_LONG,
- * MFMA_LONG_SPLIT (the same layout), or AUTO = the split operand, on
- * MFMA_LONG_SPLIT where m2rnn_pick_algo would take it, else MFMA_SPLIT. */
+ * MFMA_LONG_SPLIT (the same layout), or AUTO = the split operand: MFMA_LONG_SPLIT
+ * where m2rnn_pick_algo takes the latency-oriented kernel (MFMA_LONG_F16), else
+ * MFMA_SPLIT. The fp16-operand families are NOT_SUPPORTED here. */
 m2rnn_status m2rnn_fwd_save(const void* k, const void* v, const void* q, const void* f, const void* W,
                             const float* H0, float* y, float* H_T, void* saved,
                             int B, int H, int T, int K, int V, m2rnn_dtype in_dtype,
@@ -255,7 +256,8 @@ m2rnn_status m2rnn_bwd(const void* k, const void* v, const void* q, const void* 
  * MFMA_SPLIT: one wave per 16-row tile; MFMA_LONG, MFMA_LONG_SPLIT: a workgroup
  * of V/32 waves per tile exchanging dA through LDS every step (few tiles, long
  * sequences), its dv and df sums over a unit's tiles added in tile order by a
- * second kernel; AUTO: MFMA_LONG_SPLIT where m2rnn_pick_algo would take it.
+ * second kernel; AUTO: MFMA_LONG_SPLIT where m2rnn_pick_algo takes the
+ * latency-oriented kernel (MFMA_LONG_F16), else MFMA_SPLIT.
  * Either kernel reads the `saved` of either forward family, and every output is
  * deterministic. NOT_SUPPORTED for other families. */
 m2rnn_status m2rnn_bwd_algo(const void* k, const void* v, const void* q, const void* f, const void* W,
